@@ -1,0 +1,128 @@
+"""CPU oracle for paged-KV decode attention and the KV-append slot write.
+
+TEST INFRASTRUCTURE: only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` use this package.  The HIP library never
+imports, links or calls it, and it shares no code with the library.
+
+``pa_oracle.c`` is the float64 definition (its header states it and the
+passages it follows); this module builds it with gcc, loads it with ctypes
+and marshals torch/numpy host arrays into it.  ``dense.py`` is an
+independent NumPy check used to pin the oracle.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle (gcc -O2, no fast-math) in place; returns the .so path."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-std=c11", "-Wall",
+                           "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.oracle_write_kv.argtypes = [P, P, P, P, P, I64, I64, I, I, I, I]
+        lib.oracle_write_kv.restype = I
+        lib.oracle_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, I, I, I, I, I, I, I, P, I64, I]
+        lib.oracle_decode.restype = I
+        lib.oracle_widen.argtypes = [P, I64, I, P]
+        lib.oracle_widen.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(x):
+    if isinstance(x, torch.Tensor):
+        assert x.device.type == "cpu" and x.is_contiguous()
+        return ctypes.c_void_p(x.data_ptr())
+    assert isinstance(x, np.ndarray) and x.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(x.ctypes.data)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def widen(x: torch.Tensor) -> np.ndarray:
+    """The oracle's exact widening of a stored tensor to float64 (flattened)."""
+    x = x.contiguous()
+    out = np.empty(x.numel(), dtype=np.float64)
+    _load().oracle_widen(_ptr(x), x.numel(), _DTYPE_CODE[x.dtype], _ptr(out))
+    return out
+
+
+def write_kv(k_new: torch.Tensor, v_new: torch.Tensor, slots: np.ndarray,
+             k_pool: torch.Tensor, v_pool: torch.Tensor, *, num_blocks: int, B: int) -> None:
+    """Scatter [T, Hkv, D] rows into flat host pools in place (float64-free: bit copies)."""
+    T, Hkv, D = k_new.shape
+    slots = np.ascontiguousarray(slots, dtype=np.int64)
+    assert slots.shape == (T,) and v_new.shape == k_new.shape
+    assert k_pool.dtype == k_new.dtype == v_pool.dtype == v_new.dtype
+    rc = _load().oracle_write_kv(_ptr(k_new.contiguous()), _ptr(v_new.contiguous()), _ptr(slots),
+                                 _ptr(k_pool), _ptr(v_pool), T, num_blocks, B, Hkv, D,
+                                 _DTYPE_CODE[k_new.dtype])
+    if rc:
+        raise ValueError("oracle_write_kv: bad argument")
+
+
+def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: np.ndarray,
+           context_lens: np.ndarray, scale: float, *, Hkv: int, B: int,
+           pairs: np.ndarray | None = None, threads: int | None = None) -> np.ndarray:
+    """float64 attention output: [S, Hq, D], or [len(pairs), D] for (s, h) pairs."""
+    S, Hq, D = q.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    assert bt.shape[0] == S and ctx.shape == (S,)
+    if pairs is not None:
+        pairs = np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)
+        out = np.empty((pairs.shape[0], D), dtype=np.float64)
+        pp, npairs = _ptr(pairs), pairs.shape[0]
+    else:
+        out = np.empty((S, Hq, D), dtype=np.float64)
+        pp, npairs = None, 0
+    rc = _load().oracle_decode(_ptr(q.contiguous()), _ptr(k_pool), _ptr(v_pool), _ptr(bt), _ptr(ctx),
+                               float(np.float32(scale)), _ptr(out), S, Hq, Hkv, D, B, bt.shape[1],
+                               _DTYPE_CODE[q.dtype], pp, npairs, threads or default_threads())
+    if rc:
+        raise ValueError("oracle_decode: bad argument")
+    return out
+
+
+def build_pools(case):
+    """Flat host K/V pools after writing every token of ``case`` (prefill, then the new tokens)."""
+    k_pool, v_pool = case.nan_pool(), case.nan_pool()
+    write_kv(case.k_prefill, case.v_prefill, case.slot_prefill, k_pool, v_pool,
+             num_blocks=case.num_blocks, B=case.B)
+    write_kv(case.k_new, case.v_new, case.slot_new, k_pool, v_pool, num_blocks=case.num_blocks, B=case.B)
+    return k_pool, v_pool
+
+
+def decode_case(case, k_pool=None, v_pool=None, pairs=None, threads=None) -> np.ndarray:
+    """The oracle's answer for one case (pools built by the oracle's own write if not given)."""
+    if k_pool is None:
+        k_pool, v_pool = build_pools(case)
+    return decode(case.q, k_pool, v_pool, case.block_tables, case.context_lens, case.scale,
+                  Hkv=case.Hkv, B=case.B, pairs=pairs, threads=threads)

@@ -1,0 +1,251 @@
+/*
+ * Plain, slow, float64 CPU oracle for paged-KV decode attention and for the
+ * KV-append slot write.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check
+ * and the CPU-baseline leg of the benchmark call it; the library never does.
+ * It shares no code, header or constant with the HIP library.
+ *
+ * What it computes (the plain definition, not the fast algorithm):
+ *
+ *  write: every token i with slot >= 0 goes to physical block slot / B at
+ *    offset slot % B, for every kv-head: its K row and V row are copied there
+ *    bit for bit; nothing else in the pools changes.  Tokens are taken in
+ *    index order.  (ForgeLLM README, feature list: physical KV blocks owned
+ *    through per-request logical block tables; LLM-Inference-Engine README,
+ *    request-journey figure: fixed-size blocks handed out per request.)
+ *
+ *  decode: for sequence s and query head h, with kv-head g = h / G
+ *    (grouped-query attention, ForgeLLM README feature list: query heads share
+ *    a kv-head in contiguous groups of G) and L = context_lens[s]:
+ *      for every logical position t < L, the K and V rows live in physical
+ *      block block_tables[s][t / B] at offset t % B (ForgeLLM README, feature
+ *      list: decode attention reads the physical blocks through the block
+ *      table, never a padded K/V);
+ *      z_t = scale * sum_d q[d] * k_t[d]          (sum over d in order)
+ *      m   = max_t z_t,  w_t = exp(z_t - m)
+ *      out = (sum_t w_t * v_t) / (sum_t w_t)      (sums over t in order)
+ *    and out = 0 when L = 0.  Only positions t < L are read (the decode token
+ *    is the newest position, so the causal mask is exactly t < L).  All
+ *    arithmetic is double; stored values are widened exactly.
+ *
+ * Pool layout.  The pages fix none; this is the layout documented for the
+ * library's caller.  With X = 16 / element_bytes,
+ *    K pool: [num_blocks][Hkv][D / X][B][X]   (16-byte groups of a row, token-minor)
+ *    V pool: [num_blocks][Hkv][D][B]          (a tile is V transposed)
+ * so element (block p, kv-head g, offset o, dim d) sits at
+ *    K: (((p*Hkv + g)*(D/X) + d/X)*B + o)*X + d%X
+ *    V: ((p*Hkv + g)*D + d)*B + o
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+
+static int elt_bytes(int dtype) { return dtype == OR_F32 ? 4 : 2; }
+
+/* IEEE 754 binary16 -> double, from the format's definition. */
+static double half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the top half of an IEEE binary32. */
+static double bf16_to_double(uint16_t b) {
+    uint32_t bits = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &bits, 4);
+    return (double)f;
+}
+
+static double widen(const void* base, size_t idx, int dtype) {
+    if (dtype == OR_F32) return (double)((const float*)base)[idx];
+    uint16_t raw = ((const uint16_t*)base)[idx];
+    return dtype == OR_F16 ? half_to_double(raw) : bf16_to_double(raw);
+}
+
+static size_t k_index(int64_t p, int g, int o, int d, int Hkv, int B, int D, int X) {
+    return ((((size_t)p * Hkv + g) * (size_t)(D / X) + (size_t)(d / X)) * (size_t)B + (size_t)o) * (size_t)X +
+           (size_t)(d % X);
+}
+
+static size_t v_index(int64_t p, int g, int o, int d, int Hkv, int B, int D) {
+    return (((size_t)p * Hkv + g) * (size_t)D + (size_t)d) * (size_t)B + (size_t)o;
+}
+
+/* Returns 0, or -1 on a bad argument. */
+int oracle_write_kv(const void* k_new, const void* v_new, const int64_t* slot, void* k_pool, void* v_pool,
+                    int64_t num_tokens, int64_t num_blocks, int B, int Hkv, int D, int dtype) {
+    int eb = elt_bytes(dtype);
+    int X = 16 / eb;
+    if (B <= 0 || Hkv <= 0 || D <= 0 || D % X) return -1;
+    for (int64_t i = 0; i < num_tokens; ++i) {
+        int64_t sl = slot[i];
+        if (sl < 0) continue;
+        int64_t p = sl / B;
+        int o = (int)(sl % B);
+        if (p >= num_blocks) return -1;
+        for (int g = 0; g < Hkv; ++g) {
+            for (int d = 0; d < D; ++d) {
+                size_t src = ((size_t)i * Hkv + g) * (size_t)D + (size_t)d;
+                memcpy((char*)k_pool + k_index(p, g, o, d, Hkv, B, D, X) * eb, (const char*)k_new + src * eb, eb);
+                memcpy((char*)v_pool + v_index(p, g, o, d, Hkv, B, D) * eb, (const char*)v_new + src * eb, eb);
+            }
+        }
+    }
+    return 0;
+}
+
+typedef struct {
+    const void *q, *k_pool, *v_pool;
+    const int32_t *bt, *ctx;
+    double scale;
+    int S, Hq, Hkv, D, B, maxblk, dtype;
+    const int32_t* pairs; /* (s, h) pairs to compute, or NULL for all */
+    int64_t npairs;
+    double* out; /* [npairs][D] */
+    int64_t first, last;
+    int status;
+} job_t;
+
+/* One (s, h): the definition written out. */
+static int attend_one(const job_t* J, int s, int h, double* out_row) {
+    int G = J->Hq / J->Hkv;
+    int g = h / G;
+    int X = 16 / elt_bytes(J->dtype);
+    int L = J->ctx[s];
+    int D = J->D;
+    if (L < 0 || L > J->maxblk * J->B) return -1;
+    for (int d = 0; d < D; ++d) out_row[d] = 0.0;
+    if (L == 0) return 0;
+
+    double* q = malloc(sizeof(double) * D);
+    double* z = malloc(sizeof(double) * L);
+    if (!q || !z) {
+        free(q);
+        free(z);
+        return -1;
+    }
+    for (int d = 0; d < D; ++d) q[d] = widen(J->q, ((size_t)s * J->Hq + h) * D + d, J->dtype);
+
+    /* logits through the block table */
+    for (int t = 0; t < L; ++t) {
+        int64_t p = J->bt[(size_t)s * J->maxblk + t / J->B];
+        int o = t % J->B;
+        double dot = 0.0;
+        for (int d = 0; d < D; ++d) dot += q[d] * widen(J->k_pool, k_index(p, g, o, d, J->Hkv, J->B, D, X), J->dtype);
+        z[t] = J->scale * dot;
+    }
+    double m = z[0];
+    for (int t = 1; t < L; ++t)
+        if (z[t] > m) m = z[t];
+
+    double den = 0.0;
+    for (int t = 0; t < L; ++t) {
+        double w = exp(z[t] - m);
+        den += w;
+        int64_t p = J->bt[(size_t)s * J->maxblk + t / J->B];
+        int o = t % J->B;
+        for (int d = 0; d < D; ++d) out_row[d] += w * widen(J->v_pool, v_index(p, g, o, d, J->Hkv, J->B, D), J->dtype);
+    }
+    for (int d = 0; d < D; ++d) out_row[d] /= den;
+    free(q);
+    free(z);
+    return 0;
+}
+
+static void* run_job(void* arg) {
+    job_t* J = (job_t*)arg;
+    for (int64_t k = J->first; k < J->last; ++k) {
+        int s, h;
+        if (J->pairs) {
+            s = J->pairs[2 * k];
+            h = J->pairs[2 * k + 1];
+        } else {
+            s = (int)(k / J->Hq);
+            h = (int)(k % J->Hq);
+        }
+        if (s < 0 || s >= J->S || h < 0 || h >= J->Hq || attend_one(J, s, h, J->out + (size_t)k * J->D)) {
+            J->status = -1;
+            return NULL;
+        }
+    }
+    return NULL;
+}
+
+/*
+ * out: double [npairs][D] for the listed (s, h) pairs (pairs = int32 [npairs][2]),
+ * or [S][Hq][D] when pairs is NULL (npairs ignored).  Work is split over
+ * nthreads threads by (s, h); each output row is computed by one thread in the
+ * fixed order above, so the result does not depend on nthreads.
+ */
+int oracle_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                  const int32_t* context_lens, float scale, double* out, int S, int Hq, int Hkv, int D, int B,
+                  int max_blocks_per_seq, int dtype, const int32_t* pairs, int64_t npairs, int nthreads) {
+    if (Hkv <= 0 || Hq % Hkv || D <= 0 || B <= 0 || D % (16 / elt_bytes(dtype))) return -1;
+    int64_t n = pairs ? npairs : (int64_t)S * Hq;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > n) nthreads = n > 0 ? (int)n : 1;
+    job_t* jobs = calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t* th = calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    for (int i = 0; i < nthreads; ++i) {
+        job_t* J = &jobs[i];
+        J->q = q;
+        J->k_pool = k_pool;
+        J->v_pool = v_pool;
+        J->bt = block_tables;
+        J->ctx = context_lens;
+        J->scale = (double)scale;
+        J->S = S;
+        J->Hq = Hq;
+        J->Hkv = Hkv;
+        J->D = D;
+        J->B = B;
+        J->maxblk = max_blocks_per_seq;
+        J->dtype = dtype;
+        J->pairs = pairs;
+        J->npairs = npairs;
+        J->out = out;
+        J->first = n * i / nthreads;
+        J->last = n * (i + 1) / nthreads;
+    }
+    int started = 0;
+    for (int i = 1; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, run_job, &jobs[i])) break;
+        started = i;
+    }
+    run_job(&jobs[0]);
+    int status = jobs[0].status;
+    for (int i = 1; i <= started; ++i) {
+        pthread_join(th[i], NULL);
+        if (jobs[i].status) status = jobs[i].status;
+    }
+    /* threads that failed to start: run their share here */
+    for (int i = started + 1; i < nthreads; ++i) {
+        run_job(&jobs[i]);
+        if (jobs[i].status) status = jobs[i].status;
+    }
+    free(jobs);
+    free(th);
+    return status;
+}
+
+/* Exposes the element widening on its own, so it can be checked against other converters. */
+void oracle_widen(const void* src, int64_t n, int dtype, double* dst) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = widen(src, (size_t)i, dtype);
+}
