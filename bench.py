@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X.
+
+A step is one pass of the whole path over one batch: the KV append of one new
+token per sequence (pa_write_kv) followed by paged decode attention
+(pa_decode).  The default workload is the Llama-3-8B-shaped layer: 64
+sequences, 32 query / 8 kv heads, head_dim 128, block 16, bf16, context
+lengths uniform on [512, 4096], shuffled blocks (seed 3).
+
+Steps rotate over several "layers", each with its own K/V pools, so that the
+bytes a step reads are not left in the 256 MB last-level cache by the step
+before (as in a real model, where every layer has its own cache).  Inputs are
+resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is the algorithmic bytes of a step (K/V rows
+read, q read, out written, block-table entries and lengths, and the append's
+read+write) divided by the step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and μs per layer-step"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def setup_layers(case, layers, device, num_workers):
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+    from paged_kv_decode_slot_amd import workloads as W
+
+    dt = W.DTYPES[case.dtype]
+    q = case.q.to(device)
+    bt = torch.from_numpy(case.block_tables).to(device)
+    ctx = torch.from_numpy(case.context_lens).to(device)
+    k_new, v_new = case.k_new.to(device), case.v_new.to(device)
+    slot_new = torch.from_numpy(case.slot_new).to(device)
+    ints = torch.int32 if case.elt == 4 else torch.int16
+    k0, v0 = pa.new_cache(case.num_blocks, case.B, case.Hkv, case.D, dt, device)
+    k0.view(ints).fill_(W.NAN_BITS[case.dtype])
+    v0.view(ints).fill_(W.NAN_BITS[case.dtype])
+    if case.k_prefill.shape[0]:
+        pa.write_kv(case.k_prefill.to(device), case.v_prefill.to(device),
+                    torch.from_numpy(case.slot_prefill).to(device), k0, v0)
+    steps = []
+    for i in range(layers):
+        kc, vc = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
+        out = torch.empty_like(q)
+        steps.append((pa.prepare_write_kv(k_new, v_new, slot_new, kc, vc),
+                      pa.prepare_decode(q, kc, vc, bt, ctx, case.scale, out, num_workers=num_workers)))
+    torch.cuda.synchronize()
+    return steps
+
+
+def time_steps(steps, n_steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        w, d = steps[i % len(steps)]
+        w()
+        d()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        w, d = steps[i % len(steps)]
+        ev[i][0].record()
+        w()
+        ev[i][1].record()
+        d()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_write = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_steps)]  # us
+    t_decode = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(n_steps)]
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
+    return t_write, t_decode, total_ms, wall
+
+
+def pct(xs, p):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))]
+
+
+def measure(n, args, device):
+    from paged_kv_decode_slot_amd import workloads as W
+
+    t = time.perf_counter()
+    case = W.config_case(n)
+    log(f"[bench] workload {n}: inputs drawn in {time.perf_counter() - t:.1f}s")
+    layer_bytes = 2 * case.pool_numel * case.elt
+    layers = args.layers or max(2, math.ceil(2 * 2**30 / layer_bytes))
+    steps = setup_layers(case, layers, device, args.workers)
+    log(f"[bench] workload {n}: {layers} layers of {layer_bytes / 1e9:.2f} GB; timing {args.steps} steps")
+    t_write, t_decode, total_ms, wall = time_steps(steps, args.steps, args.warmup)
+    dec_b, wr_b = W.decode_bytes(case), W.write_bytes(case)
+    ms_per_step = total_ms / args.steps
+    dec_mean = statistics.fmean(t_decode)
+    res = dict(
+        case=case,
+        ms_per_step=ms_per_step,
+        step_gbs=(dec_b + wr_b) / (ms_per_step * 1e-3) / 1e9,
+        decode_bytes=dec_b,
+        write_bytes=wr_b,
+        t_decode_us=dict(mean=dec_mean, p10=pct(t_decode, 10), p50=pct(t_decode, 50), p90=pct(t_decode, 90)),
+        t_write_us=dict(mean=statistics.fmean(t_write), p50=pct(t_write, 50)),
+        t_layer_us_p50=pct([a + b for a, b in zip(t_write, t_decode)], 50),
+        decode_gbs=dec_b / (dec_mean * 1e-6) / 1e9,
+        seq_heads_per_s=case.S * case.Hq / (dec_mean * 1e-6),
+        layers=layers,
+        wall_s=wall,
+    )
+    return res
+
+
+def cpu_baseline(case, min_seconds):
+    import oracle
+    from paged_kv_decode_slot_amd import workloads as W
+
+    kp, vp = case.nan_pool(), case.nan_pool()
+    oracle.write_kv(case.k_prefill, case.v_prefill, case.slot_prefill, kp, vp, num_blocks=case.num_blocks, B=case.B)
+    threads = oracle.default_threads()
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds or reps == 0:
+        t = time.perf_counter()
+        oracle.write_kv(case.k_new, case.v_new, case.slot_new, kp, vp, num_blocks=case.num_blocks, B=case.B)
+        oracle.decode(case.q, kp, vp, case.block_tables, case.context_lens, case.scale, Hkv=case.Hkv, B=case.B,
+                      threads=threads)
+        t_total += time.perf_counter() - t
+        reps += 1
+    per_step = t_total / reps
+    gbs = (W.decode_bytes(case) + W.write_bytes(case)) / per_step / 1e9
+    return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
+                sample=f"the whole workload (append + decode of all {case.S} sequences), {reps} reps, "
+                       f"{per_step * 1e3:.1f} ms per step, float64 C oracle")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3, help="workload 1-5 (default 3)")
+    ap.add_argument("--also", default="4", help="comma list of extra workloads reported under 'other'")
+    ap.add_argument("--layers", type=int, default=0, help="distinct K/V pools to rotate over (0: enough for 2 GiB)")
+    ap.add_argument("--workers", type=int, default=0, help="decode work split (0 automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this path runs on one GPU (asked for {max(args.gpus, world)}); "
+              "a multi-GPU run is not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+    from paged_kv_decode_slot_amd import workloads as W
+
+    pa.lib()  # fail loudly before any setup if the library is missing
+    device = torch.device("cuda:0")
+    main_res = measure(args.config, args, device)
+    case = main_res.pop("case")
+
+    other = {}
+    for n in [int(x) for x in args.also.split(",") if x.strip()]:
+        if n == args.config:
+            continue
+        r = measure(n, args, device)
+        c = r.pop("case")
+        other[f"C{n}"] = dict(workload=W.CONFIGS[n]["name"], t_decode_us_mean=round(r["t_decode_us"]["mean"], 2),
+                              t_decode_us_p50=round(r["t_decode_us"]["p50"], 2),
+                              t_layer_us_p50=round(r["t_layer_us_p50"], 2),
+                              decode_gbs=round(r["decode_gbs"], 1),
+                              decode_frac_of_peak=round(r["decode_gbs"] / PEAK_HBM_GBS, 4),
+                              seq_heads_per_s=round(r["seq_heads_per_s"]), layers=r["layers"],
+                              decode_bytes=r["decode_bytes"], context_tokens=int(c.context_lens.sum()))
+        del c, r
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the host")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    dec_us = main_res["t_decode_us"]["mean"]
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded; no model weights or datasets)",
+        "config": {
+            "workload": W.CONFIGS[args.config]["name"],
+            "seqs": case.S, "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,
+            "block_size": case.B, "context_tokens": int(case.context_lens.sum()),
+            "step": "pa_write_kv of one token per sequence, then pa_decode",
+            "layers_rotated": main_res["layers"], "workers": args.workers,
+        },
+        "roofline": {
+            "kernel": "pa_decode (decode_kernel + merge_kernel)",
+            "bound": "hbm",
+            "achieved": round(main_res["decode_gbs"], 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(main_res["decode_gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": main_res["decode_bytes"],
+            "launch_us_mean": round(dec_us, 2),
+        },
+        "cpu_baseline": cpu,
+        "detail": {
+            "t_decode_us": {k: round(v, 2) for k, v in main_res["t_decode_us"].items()},
+            "t_write_us": {k: round(v, 2) for k, v in main_res["t_write_us"].items()},
+            "t_layer_us_p50": round(main_res["t_layer_us_p50"], 2),
+            "decode_gbs": round(main_res["decode_gbs"], 1),
+            "seq_heads_per_s": round(main_res["seq_heads_per_s"]),
+            "step_bytes": main_res["decode_bytes"] + main_res["write_bytes"],
+            "other": other,
+        },
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

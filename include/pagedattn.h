@@ -1,0 +1,157 @@
+/*
+ * libpagedattn: decode-step attention over a paged (block-table) KV cache,
+ * and the KV-append write that places each new token's K/V in its slot,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Where the operations come from:
+ *  - ForgeLLM README (LLM-inference-server), feature list: the KV cache is a
+ *    pool of physical blocks, each request owns a logical block table that
+ *    maps its j-th block to a physical one, and decode attention reads the
+ *    physical blocks straight through that table with an online softmax,
+ *    never assembling a padded batch-wide K/V; the decoder uses grouped-query
+ *    attention.
+ *  - LLM-Inference-Engine README, request-journey figure and the "why paged
+ *    KV cache" paragraph: fixed-size blocks are preallocated and handed to a
+ *    request on demand as it grows; the "why dynamic injection" paragraph:
+ *    decode is memory-bound.
+ *
+ * Conventions shared by every call
+ *  - All pointers to tensors are DEVICE pointers; descriptors are HOST
+ *    pointers.  Every tensor is dense and row-major.
+ *  - One element type (pa_dtype_t) for q, out, the caches and new K/V rows.
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *    void*; NULL is the null stream).  They never synchronise the host,
+ *    never allocate, keep no pointer after returning and hold no state
+ *    beyond a per-device compute-unit count, so they are reentrant.
+ *  - The caller owns every buffer.  Errors come back as pa_status_t; nothing
+ *    is thrown across the ABI.  Arguments are checked on the host before any
+ *    launch; device data (slots, block ids, lengths) cannot be checked
+ *    without a synchronisation and is a precondition.  Out-of-range device
+ *    values are clamped inside the kernels so they cannot fault, but the
+ *    results are then unspecified.
+ *
+ * Cache layout (the same pool geometry for K and V; X = 16 / element bytes,
+ * so X = 4 for f32 and 8 for f16/bf16):
+ *    K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
+ *    V pool: [num_blocks][num_kv_heads][head_dim][block_size]
+ *  Token `o` of physical block `p`, kv-head `g`, dimension `d` is
+ *    K[p][g][d / X][o][d % X]   and   V[p][g][d][o].
+ *  One (block, kv-head) tile is block_size * head_dim contiguous elements in
+ *  either pool.  A slot is p * block_size + o.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, Hq not a multiple of Hkv */
+    PA_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
+    PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+    PA_ERR_HIP = 4          /* a HIP runtime call or a launch failed */
+} pa_status_t;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+
+/* Geometry of a K/V pool pair. */
+typedef struct pa_cache_desc {
+    int32_t num_blocks;   /* physical blocks in each pool, > 0 */
+    int32_t block_size;   /* tokens per block: 16 or 32 */
+    int32_t num_kv_heads; /* Hkv > 0 */
+    int32_t head_dim;     /* D: 64 or 128 */
+    int32_t dtype;        /* a pa_dtype_t */
+} pa_cache_desc_t;
+
+typedef void* pa_stream_t; /* a hipStream_t */
+
+/*
+ * KV append: for every token i < num_tokens with slot_mapping[i] >= 0, copy
+ * k_new[i][g][:] and v_new[i][g][:] (every kv-head g) into physical block
+ * slot / block_size at offset slot % block_size of k_cache / v_cache, bit for
+ * bit.  A negative slot marks a padding token: nothing is written for it.
+ * No other cache byte changes.
+ *   k_new, v_new : [num_tokens][num_kv_heads][head_dim], 16-byte aligned
+ *   slot_mapping : int64 [num_tokens], 8-byte aligned
+ *   k_cache, v_cache : pools in the layout above, 16-byte aligned
+ * Preconditions (unchecked): slot < num_blocks * block_size; no two tokens
+ * of one call share a non-negative slot.  A slot past the pool is skipped.
+ * num_tokens == 0 is a no-op.
+ */
+pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
+                        void* v_cache, int32_t num_tokens, const pa_cache_desc_t* cache, pa_stream_t stream);
+
+/*
+ * Decode attention, one query token per sequence: for sequence s < num_seqs
+ * and query head h < num_q_heads, with G = num_q_heads / num_kv_heads,
+ * kv-head g = h / G and L = context_lens[s],
+ *   out[s][h][:] = sum_{t<L} softmax_t(scale * q[s][h][:] . K_t) * V_t
+ * where K_t, V_t are the rows of logical position t, found in physical block
+ * block_tables[s][t / block_size] at offset t % block_size.  L counts the
+ * token being decoded (its K/V must already be written), and only positions
+ * t < L are read: block-table entries past ceil(L / block_size) and slots
+ * past L in the last block may hold anything, NaN included.  L == 0 gives
+ * out = 0.  Arithmetic is fp32; out is rounded to nearest-even once.
+ *   q, out        : [num_seqs][num_q_heads][head_dim], 16-byte aligned; out
+ *                   must not overlap any input
+ *   block_tables  : int32 [num_seqs][max_blocks_per_seq], 4-byte aligned
+ *   context_lens  : int32 [num_seqs], 4-byte aligned
+ *   workspace     : device scratch of at least pa_decode_workspace_bytes(...)
+ *                   bytes, 256-byte aligned (may be NULL when that is 0);
+ *                   its contents need no initialisation and are clobbered
+ * Supported: 1 <= G <= 16, head_dim 64/128, block_size 16/32, num_seqs <= 4096.
+ * Preconditions (unchecked): 0 <= L <= max_blocks_per_seq * block_size and
+ * 0 <= block_tables[s][j] < num_blocks for j < ceil(L / block_size).
+ * The result depends only on logical positions: it is bitwise the same
+ * for any physical placement and from run to run.  num_seqs == 0 is a no-op.
+ */
+pa_status_t pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
+                      size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * Workspace bytes pa_decode needs for these shapes on the current device
+ * (0 means none).  Returns 0 as well for arguments pa_decode would reject.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 const pa_cache_desc_t* cache);
+
+/*
+ * pa_decode with the work split chosen by the caller:
+ *   num_workers == 0  : automatic (what pa_decode does)
+ *   num_workers == -1 : one wavefront per (sequence, kv-head) over its whole
+ *                       context; no partial results, no merge
+ *   num_workers  > 0  : the logical blocks of all (sequence, kv-head) pairs
+ *                       are dealt to that many wavefronts in equal contiguous
+ *                       runs; pairs cut between runs are merged by a
+ *                       log-sum-exp reduction
+ * Every choice computes the same function; results agree within rounding.
+ */
+pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
+                         size_t workspace_bytes, int32_t num_workers, pa_stream_t stream);
+
+/* Workspace bytes pa_decode_ex needs for that num_workers. */
+size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                    const pa_cache_desc_t* cache, int32_t num_workers);
+
+/* Static, human-readable name of a status. */
+const char* pa_status_string(pa_status_t status);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -60,10 +60,13 @@ def _ptr(x):
 
 
 def default_threads() -> int:
+    """Host threads to use: the CPU affinity set, capped by OMP_NUM_THREADS when that is set."""
     try:
-        return len(os.sched_getaffinity(0))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(cap))) if cap.isdigit() and int(cap) > 0 else n
 
 
 def widen(x: torch.Tensor) -> np.ndarray:

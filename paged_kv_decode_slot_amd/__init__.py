@@ -1,0 +1,20 @@
+"""Paged-KV decode attention and KV append on MI355X (gfx950).
+
+The computation lives in the HIP library ``libpagedattn.so`` (C ABI declared
+in ``include/pagedattn.h``); this package is its thin Python binding plus the
+seeded workload generator used by the tests and the benchmark.
+"""
+from .binding import (  # noqa: F401
+    CacheDesc,
+    PagedAttnError,
+    cache_desc,
+    cache_shapes,
+    decode,
+    lib,
+    library_path,
+    new_cache,
+    prepare_decode,
+    prepare_write_kv,
+    workspace_bytes,
+    write_kv,
+)

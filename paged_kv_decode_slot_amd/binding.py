@@ -1,0 +1,235 @@
+"""Thin Python binding of libpagedattn (ctypes).
+
+Argument marshalling only: shapes, dtypes, devices and the current HIP stream
+are checked and passed through; every step of the computation runs in the
+library's kernels.  There is no fallback: if the library is not built,
+every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+_ELT = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
+
+EXPORTS = (
+    "pa_write_kv",
+    "pa_decode",
+    "pa_decode_ex",
+    "pa_decode_workspace_bytes",
+    "pa_decode_workspace_bytes_ex",
+    "pa_status_string",
+    "pa_abi_version",
+)
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m paged_kv_decode_slot_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        DP = ctypes.POINTER(CacheDesc)
+        L.pa_write_kv.argtypes = [P, P, P, P, P, I32, DP, P]
+        L.pa_write_kv.restype = ctypes.c_int
+        L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, P]
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_ex.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, I32, P]
+        L.pa_decode_ex.restype = ctypes.c_int
+        L.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, DP]
+        L.pa_decode_workspace_bytes.restype = SZ
+        L.pa_decode_workspace_bytes_ex.argtypes = [I32, I32, I32, DP, I32]
+        L.pa_decode_workspace_bytes_ex.restype = SZ
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_abi_version.argtypes = []
+        L.pa_abi_version.restype = I32
+        _lib = L
+    return _lib
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        msg = lib().pa_status_string(status).decode()
+        if status in (PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE):
+            raise ValueError(f"{fn}: {msg} (status {status})")
+        raise PagedAttnError(fn, status, msg)
+
+
+def cache_shapes(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype):
+    """Shapes of the K and V pools in the library's layout."""
+    X = 16 // _ELT[dtype]
+    return ((num_blocks, num_kv_heads, head_dim // X, block_size, X),
+            (num_blocks, num_kv_heads, head_dim, block_size))
+
+
+def new_cache(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+              dtype: torch.dtype, device) -> tuple[torch.Tensor, torch.Tensor]:
+    """Uninitialised K and V pools (torch device memory) in the library's layout."""
+    ks, vs = cache_shapes(num_blocks, block_size, num_kv_heads, head_dim, dtype)
+    return (torch.empty(ks, dtype=dtype, device=device), torch.empty(vs, dtype=dtype, device=device))
+
+
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> CacheDesc:
+    """The pool geometry, read from the pools' shapes (which must match the layout)."""
+    if k_cache.dim() != 5 or v_cache.dim() != 4:
+        raise ValueError("k_cache must be [NB, Hkv, D/X, B, X] and v_cache [NB, Hkv, D, B]")
+    NB, Hkv, DX, B, X = k_cache.shape
+    if k_cache.dtype not in _DTYPE_CODE or v_cache.dtype != k_cache.dtype:
+        raise ValueError("caches must share one of float32/float16/bfloat16")
+    if X * _ELT[k_cache.dtype] != 16:
+        raise ValueError("innermost K dimension must hold 16 bytes")
+    D = DX * X
+    if tuple(v_cache.shape) != (NB, Hkv, D, B):
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+    if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    return CacheDesc(NB, B, Hkv, D, _DTYPE_CODE[k_cache.dtype])
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    d = ts[0].device
+    if d.type != "cuda":
+        raise ValueError("tensors must be on a GPU")
+    for t in ts:
+        if t.device != d:
+            raise ValueError("all tensors must be on one device")
+    return d
+
+
+def _write_args(k_new, v_new, slot_mapping, k_cache, v_cache):
+    desc = cache_desc(k_cache, v_cache)
+    dev = _dev(k_new, v_new, slot_mapping, k_cache, v_cache)
+    if k_new.shape != v_new.shape or k_new.dim() != 3 or tuple(k_new.shape[1:]) != (desc.num_kv_heads, desc.head_dim):
+        raise ValueError("k_new/v_new must be [T, Hkv, D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise ValueError("k_new/v_new dtype must match the caches")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (k_new.shape[0],):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if not (k_new.is_contiguous() and v_new.is_contiguous() and slot_mapping.is_contiguous()):
+        raise ValueError("inputs must be contiguous")
+    args = (k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            int(k_new.shape[0]), ctypes.byref(desc), _stream(dev))
+    return dev, args, (k_new, v_new, slot_mapping, k_cache, v_cache, desc)
+
+
+def write_kv(k_new: torch.Tensor, v_new: torch.Tensor, slot_mapping: torch.Tensor,
+             k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    """Append: copy each token's K/V rows ([T, Hkv, D]) into slot_mapping[t] (int64; < 0 skips)."""
+    dev, args, _keep = _write_args(k_new, v_new, slot_mapping, k_cache, v_cache)
+    with torch.cuda.device(dev):
+        st = lib().pa_write_kv(*args)
+    _check("pa_write_kv", st)
+
+
+def workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, desc: CacheDesc,
+                    num_workers: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes_ex(num_seqs, num_q_heads, max_blocks_per_seq,
+                                                  ctypes.byref(desc), num_workers))
+
+
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_workers, workspace):
+    desc = cache_desc(k_cache, v_cache)
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim or q.dtype != k_cache.dtype or not q.is_contiguous():
+        raise ValueError("q must be contiguous [S, Hq, D] in the cache dtype")
+    S, Hq, D = q.shape
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [S, max_blocks_per_seq]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,) or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [S]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be contiguous and shaped like q")
+    maxblk = int(block_tables.shape[1])
+    need = workspace_bytes(S, Hq, maxblk, desc, num_workers)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor on the same device")
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+            ctypes.c_float(scale), out.data_ptr(), S, Hq, maxblk, ctypes.byref(desc), workspace.data_ptr(),
+            workspace.numel(), int(num_workers), _stream(dev))
+    return dev, out, args, (q, k_cache, v_cache, block_tables, context_lens, out, workspace, desc)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+           context_lens: torch.Tensor, scale: float, out: torch.Tensor | None = None, *,
+           num_workers: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention of q [S, Hq, D] over the paged caches; returns out [S, Hq, D].
+
+    num_workers: 0 automatic, -1 one wavefront per (sequence, kv-head), >0 that many.
+    workspace: optional uint8 device tensor; one is allocated when not given.
+    """
+    dev, out, args, _keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                         num_workers, workspace)
+    with torch.cuda.device(dev):
+        st = lib().pa_decode_ex(*args)
+    _check("pa_decode", st)
+    return out
+
+
+def prepare_write_kv(k_new, v_new, slot_mapping, k_cache, v_cache):
+    """Validate once; return a no-argument callable that issues the same pa_write_kv
+    on the stream that is current now (for tight loops)."""
+    _dev_, args, keep = _write_args(k_new, v_new, slot_mapping, k_cache, v_cache)
+    fn = lib().pa_write_kv
+
+    def call():
+        _check("pa_write_kv", fn(*args))
+        return keep
+
+    return call
+
+
+def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=None, *, num_workers=0,
+                   workspace=None):
+    """Validate once (allocating out and the workspace if not given); return a
+    no-argument callable that issues the same pa_decode_ex on the stream that
+    is current now, and returns out."""
+    _dev_, out, args, keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                          num_workers, workspace)
+    fn = lib().pa_decode_ex
+
+    def call():
+        _check("pa_decode", fn(*args))
+        return keep[5]
+
+    return call

@@ -1,0 +1,76 @@
+"""Shared plumbing for the GPU parity tests: both sides built from one seeded case.
+
+The GPU side fills NaN-poisoned pools with the library's own pa_write_kv; the
+oracle side fills its host pools with the oracle's own write.  Nothing the
+GPU computes feeds the oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_decode_slot_amd as pa
+from paged_kv_decode_slot_amd import workloads as W
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1.5e-2}
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+class GpuCase:
+    """Device copies of a case, with pools written by the library."""
+
+    def __init__(self, case: W.Case, device="cuda:0"):
+        self.case = case
+        dt = W.DTYPES[case.dtype]
+        self.k_cache, self.v_cache = pa.new_cache(case.num_blocks, case.B, case.Hkv, case.D, dt, device)
+        ints = torch.int32 if case.elt == 4 else torch.int16
+        self.k_cache.view(ints).fill_(W.NAN_BITS[case.dtype])
+        self.v_cache.view(ints).fill_(W.NAN_BITS[case.dtype])
+        self.q = case.q.to(device)
+        self.bt = torch.from_numpy(case.block_tables).to(device)
+        self.ctx = torch.from_numpy(case.context_lens).to(device)
+        self.k_new = case.k_new.to(device)
+        self.v_new = case.v_new.to(device)
+        self.slot_new = torch.from_numpy(case.slot_new).to(device)
+        if case.k_prefill.shape[0]:
+            pa.write_kv(case.k_prefill.to(device), case.v_prefill.to(device),
+                        torch.from_numpy(case.slot_prefill).to(device), self.k_cache, self.v_cache)
+        self.appended = False
+
+    def append(self):
+        """The decode step's KV append of the new token of every sequence."""
+        pa.write_kv(self.k_new, self.v_new, self.slot_new, self.k_cache, self.v_cache)
+        self.appended = True
+
+    def decode(self, num_workers=0, out=None):
+        assert self.appended
+        return pa.decode(self.q, self.k_cache, self.v_cache, self.bt, self.ctx, self.case.scale, out,
+                         num_workers=num_workers)
+
+
+def flat_bits(t: torch.Tensor) -> torch.Tensor:
+    """A host integer view of a tensor's bytes, so NaN payloads compare too."""
+    t = t.detach().contiguous().cpu().view(-1)
+    return t.view(torch.int32 if t.element_size() == 4 else torch.int16)
+
+
+def dev_bits(t: torch.Tensor) -> torch.Tensor:
+    """A flat integer view of a tensor's bytes, on its own device."""
+    t = t.contiguous().view(-1)
+    return t.view({4: torch.int32, 2: torch.int16, 1: torch.uint8}[t.element_size()])
+
+
+def oracle_pools(case: W.Case):
+    return oracle.build_pools(case)
+
+
+def max_abs_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
+    got = gpu_out.detach().float().cpu().double().numpy()
+    assert got.shape == ref.shape
+    if not np.isfinite(got).all():
+        return float("inf")
+    return float(np.abs(got - ref).max()) if got.size else 0.0

@@ -1,0 +1,125 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_decode_slot_amd as pa
+from paged_kv_decode_slot_amd.binding import CacheDesc, EXPORTS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
+
+
+def header_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(pa_\w+)\s*\(", text))
+    return names
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == set(EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = pa.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+
+
+def test_abi_version_and_status_strings():
+    L = pa.lib()
+    assert L.pa_abi_version() == 1
+    for st in range(5):
+        assert L.pa_status_string(st)
+    assert L.pa_status_string(99) == b"unknown status"
+
+
+def _desc(**kw):
+    d = dict(num_blocks=10, block_size=16, num_kv_heads=2, head_dim=64, dtype=2)
+    d.update(kw)
+    return CacheDesc(**d)
+
+
+# fake, suitably aligned device addresses: validation never dereferences them
+A = 0x10000
+
+
+def _write(desc, *, k=A, v=A, slots=A, kc=A, vc=A, T=4):
+    return pa.lib().pa_write_kv(k, v, slots, kc, vc, T, ctypes.byref(desc) if desc is not None else None, None)
+
+
+def _decode(desc, *, q=A, kc=A, vc=A, bt=A, ctx=A, out=A, S=2, Hq=4, maxblk=3, ws=A, ws_bytes=1 << 30,
+            workers=64, scale=0.125):
+    return pa.lib().pa_decode_ex(q, kc, vc, bt, ctx, scale, out, S, Hq, maxblk,
+                                 ctypes.byref(desc) if desc is not None else None, ws, ws_bytes, workers, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(slots=None), INVALID),
+    (dict(kc=None), INVALID), (dict(vc=None), INVALID), (dict(T=-1), INVALID),
+    (dict(k=A + 8), INVALID), (dict(slots=A + 4), INVALID), (dict(vc=A + 2), INVALID),
+])
+def test_write_kv_rejects(kw, status):
+    assert _write(_desc(), **kw) == status
+
+
+def test_write_kv_zero_tokens_is_a_noop():
+    assert _write(_desc(), T=0) == OK
+
+
+@pytest.mark.parametrize("desc,status", [
+    (None, INVALID),
+    (dict(num_blocks=0), INVALID), (dict(num_kv_heads=0), INVALID), (dict(head_dim=-64), INVALID),
+    (dict(block_size=8), UNSUPPORTED), (dict(head_dim=96), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+])
+def test_cache_descriptor_checks(desc, status):
+    d = None if desc is None else _desc(**desc)
+    assert _write(d) == status
+    assert _decode(d) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INVALID), (dict(kc=None), INVALID), (dict(ctx=None), INVALID), (dict(out=None), INVALID),
+    (dict(bt=None), INVALID), (dict(q=A + 4), INVALID), (dict(out=A + 8), INVALID), (dict(bt=A + 2), INVALID),
+    (dict(Hq=3), INVALID), (dict(S=-1), INVALID), (dict(maxblk=-1), INVALID), (dict(Hq=0), INVALID),
+    (dict(Hq=34), UNSUPPORTED),  # G = 17
+    (dict(S=4097), UNSUPPORTED),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
+    (dict(workers=-2), INVALID),
+    (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=A + 16), WORKSPACE),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(_desc(), **kw) == status
+
+
+def test_decode_zero_sequences_is_a_noop():
+    assert _decode(_desc(), S=0) == OK
+
+
+def test_workspace_sizes():
+    L = pa.lib()
+    d = _desc(head_dim=128, num_kv_heads=8)
+    # one wavefront per (sequence, kv-head): no workspace
+    assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), -1) == 0
+    # stream split: prefix + 2 parts per worker of G lse values and G*D outputs
+    W, S, G, D = 100, 64, 4, 128
+    got = L.pa_decode_workspace_bytes_ex(S, 32, 256, ctypes.byref(d), W)
+    r = lambda x: (x + 255) // 256 * 256
+    assert got == r(4 * (S + 1)) + r(4 * W * 2 * G) + 4 * W * 2 * G * D
+    # rejected shapes report 0
+    assert L.pa_decode_workspace_bytes_ex(64, 33, 256, ctypes.byref(d), W) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    k, v = torch.zeros(2, 2, 8, 16, 8, dtype=torch.bfloat16), torch.zeros(2, 2, 64, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pa.write_kv(torch.zeros(1, 2, 64, dtype=torch.bfloat16), torch.zeros(1, 2, 64, dtype=torch.bfloat16),
+                    torch.zeros(1, dtype=torch.int64), k, v)

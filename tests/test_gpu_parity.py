@@ -1,0 +1,172 @@
+"""GPU parity: the HIP library against the float64 CPU oracle, through the C ABI.
+
+pa_write_kv must reproduce the oracle's pools byte for byte (NaN poison in
+every unwritten byte included); pa_decode must agree with the oracle within
+the stated bound per dtype (max-abs 1e-5 fp32, 2e-3 fp16, 1.5e-2 bf16) on
+every output element, for every work split, on all five workloads at full
+size and on small shapes that cover the edges.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_decode_slot_amd import workloads as W
+from tests.gpu_helpers import TOL, GpuCase, dev_bits, flat_bits, log, max_abs_err, oracle_pools
+
+pytestmark = pytest.mark.gpu
+
+_memo = {}
+
+
+def config_state(n):
+    """Case, GPU side (appended) and oracle pools/output of workload n; one workload held at a time."""
+    if n not in _memo:
+        _memo.clear()
+        torch.cuda.empty_cache()
+        log(f"[setup] workload {n}: drawing inputs")
+        case = W.config_case(n)
+        g = GpuCase(case)
+        g.append()
+        torch.cuda.synchronize()
+        log(f"[setup] workload {n}: oracle pools and output")
+        kp, vp = oracle_pools(case)
+        ref = oracle.decode_case(case, kp, vp)
+        _memo[n] = (case, g, kp, vp, ref)
+    return _memo[n]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_write_kv_pools_bitexact(n):
+    case, g, kp, vp, _ = config_state(n)
+    log(f"[write] workload {n}: comparing {case.pool_numel * case.elt * 2 / 1e9:.2f} GB of pool bytes")
+    assert torch.equal(flat_bits(g.k_cache), flat_bits(kp))
+    assert torch.equal(flat_bits(g.v_cache), flat_bits(vp))
+
+
+@pytest.mark.parametrize("workers", [0, -1, 7, 3000])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_decode_parity_workloads(n, workers):
+    case, g, _, _, ref = config_state(n)
+    log(f"[decode] workload {n} workers={workers}")
+    out = g.decode(num_workers=workers)
+    torch.cuda.synchronize()
+    err = max_abs_err(out, ref)
+    log(f"[decode] workload {n} workers={workers}: max abs err {err:.3e}")
+    assert err <= TOL[case.dtype]
+
+
+@pytest.mark.parametrize("n", [3, 4])
+def test_decode_leaves_caches_and_inputs_unchanged(n):
+    case, g, kp, vp, _ = config_state(n)
+    kb, vb = g.k_cache.clone(), g.v_cache.clone()
+    qb, btb, cb = g.q.clone(), g.bt.clone(), g.ctx.clone()
+    g.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(dev_bits(g.k_cache), dev_bits(kb)) and torch.equal(dev_bits(g.v_cache), dev_bits(vb))
+    assert torch.equal(dev_bits(g.q), dev_bits(qb)) and torch.equal(g.bt, btb) and torch.equal(g.ctx, cb)
+
+
+@pytest.mark.parametrize("n", [2, 3])
+def test_decode_bitwise_deterministic(n):
+    _, g, _, _, _ = config_state(n)
+    for workers in (0, -1, 123):
+        a = g.decode(num_workers=workers)
+        b = g.decode(num_workers=workers)
+        torch.cuda.synchronize()
+        assert torch.equal(dev_bits(a), dev_bits(b))
+
+
+SMALL = [
+    dict(S=5, Hq=8, Hkv=2, D=128, B=16, dtype="bf16", ctx_range=(1, 300)),
+    dict(S=3, Hq=16, Hkv=1, D=64, B=32, dtype="f16", ctx_range=(1, 200)),  # G = 16
+    dict(S=7, Hq=3, Hkv=3, D=128, B=32, dtype="bf16", ctx_range=(1, 100)),  # G = 1
+    dict(S=4, Hq=7, Hkv=1, D=128, B=16, dtype="f32", ctx_range=(1, 90)),
+    dict(S=6, Hq=4, Hkv=2, D=64, B=32, dtype="f32", ctx_range=(1, 150)),
+    dict(S=9, Hq=12, Hkv=4, D=64, B=16, dtype="f16", ctx_range=(1, 700)),
+    dict(S=8, Hq=6, Hkv=2, D=128, B=32, dtype="bf16", ctx=[0, 1, 15, 16, 17, 32, 33, 0], max_blocks_per_seq=4),
+    dict(S=6, Hq=4, Hkv=4, D=64, B=16, dtype="f32", ctx=[0, 0, 0, 1, 0, 2]),
+    dict(S=1, Hq=5, Hkv=1, D=64, B=16, dtype="bf16", ctx=[3000]),
+    dict(S=40, Hq=2, Hkv=1, D=128, B=16, dtype="f16", ctx_range=(1, 40), max_blocks_per_seq=9),
+]
+
+
+@pytest.mark.parametrize("workers", [0, -1, 1, 3, 50, 10000])
+@pytest.mark.parametrize("idx", range(len(SMALL)))
+def test_decode_parity_small_shapes(idx, workers):
+    kw = dict(SMALL[idx])
+    case = W.make_case(seed=100 + idx, **kw)
+    log(f"[small] {idx} {kw} workers={workers}")
+    g = GpuCase(case)
+    g.append()
+    kp, vp = oracle_pools(case)
+    assert torch.equal(flat_bits(g.k_cache), flat_bits(kp)) and torch.equal(flat_bits(g.v_cache), flat_bits(vp))
+    ref = oracle.decode_case(case, kp, vp)
+    out = g.decode(num_workers=workers)
+    torch.cuda.synchronize()
+    err = max_abs_err(out, ref)
+    log(f"[small] {idx} workers={workers}: max abs err {err:.3e}")
+    assert err <= TOL[case.dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_single_key_returns_v_exactly(dtype):
+    case = W.make_case(S=5, Hq=8, Hkv=2, D=64, B=16, dtype=dtype, ctx=[1, 1, 1, 1, 1], seed=7)
+    g = GpuCase(case)
+    g.append()
+    for workers in (0, -1):
+        out = g.decode(num_workers=workers).cpu()
+        expect = case.v_new.repeat_interleave(case.G, dim=1)
+        assert torch.equal(dev_bits(out), dev_bits(expect))
+
+
+def test_block_permutation_invariance_bitwise():
+    case = W.make_case(S=6, Hq=8, Hkv=2, D=128, B=16, dtype="bf16", ctx_range=(100, 900), seed=31)
+    perm = np.random.default_rng(5).permutation(case.num_blocks)
+
+    def remap(slots):
+        out = slots.copy()
+        ok = slots >= 0
+        out[ok] = perm[slots[ok] // case.B] * case.B + slots[ok] % case.B
+        return out
+
+    moved = W.Case(**{**case.__dict__, "block_tables": perm[case.block_tables].astype(np.int32),
+                      "slot_prefill": remap(case.slot_prefill), "slot_new": remap(case.slot_new)})
+    a, b = GpuCase(case), GpuCase(moved)
+    a.append()
+    b.append()
+    for workers in (0, -1, 17):
+        oa, ob = a.decode(num_workers=workers), b.decode(num_workers=workers)
+        torch.cuda.synchronize()
+        assert torch.equal(dev_bits(oa), dev_bits(ob))
+
+
+@pytest.mark.parametrize("factor", [10.0, 100.0])
+def test_large_logits_stay_finite(factor):
+    case = W.make_case(S=4, Hq=8, Hkv=2, D=128, B=16, dtype="bf16", ctx_range=(50, 400), seed=41)
+    case.q = (case.q.float() * factor).to(case.q.dtype)
+    g = GpuCase(case)
+    g.append()
+    ref = oracle.decode_case(case)
+    for workers in (0, -1, 200):
+        out = g.decode(num_workers=workers)
+        torch.cuda.synchronize()
+        assert max_abs_err(out, ref) <= TOL["bf16"]
+
+
+def test_write_kv_padding_slots_skipped():
+    case = W.make_case(S=6, Hq=4, Hkv=2, D=64, B=16, dtype="f16", ctx=[5, 0, 9, 0, 1, 30], seed=51)
+    assert (case.slot_new < 0).sum() == 2
+    g = GpuCase(case)
+    g.append()
+    kp, vp = oracle_pools(case)
+    assert torch.equal(flat_bits(g.k_cache), flat_bits(kp)) and torch.equal(flat_bits(g.v_cache), flat_bits(vp))
+
+
+def test_zero_sequences_is_a_noop():
+    case = W.make_case(S=2, Hq=4, Hkv=2, D=64, B=16, dtype="bf16", ctx=[3, 4], seed=1)
+    g = GpuCase(case)
+    g.append()
+    import paged_kv_decode_slot_amd as pa
+    out = pa.decode(g.q[:0], g.k_cache, g.v_cache, g.bt[:0], g.ctx[:0], case.scale)
+    assert out.shape == (0, 4, 64)
