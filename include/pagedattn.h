@@ -83,7 +83,7 @@ typedef void* pa_stream_t; /* a hipStream_t */
  *   k_cache, v_cache : pools in the layout above, 16-byte aligned
  * Preconditions (unchecked): slot < num_blocks * block_size; no two tokens
  * of one call share a non-negative slot.  A slot past the pool is skipped.
- * num_tokens == 0 is a no-op.
+ * num_tokens == 0 is a no-op (pointers are then not looked at).
  */
 pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
                         void* v_cache, int32_t num_tokens, const pa_cache_desc_t* cache, pa_stream_t stream);
@@ -110,7 +110,8 @@ pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slo
  * Preconditions (unchecked): 0 <= L <= max_blocks_per_seq * block_size and
  * 0 <= block_tables[s][j] < num_blocks for j < ceil(L / block_size).
  * The result depends only on logical positions: it is bitwise the same
- * for any physical placement and from run to run.  num_seqs == 0 is a no-op.
+ * for any physical placement and from run to run.  num_seqs == 0 is a no-op
+ * (pointers are then not looked at).
  */
 pa_status_t pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,

@@ -667,11 +667,11 @@ pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slo
     pa_status_t st = check_cache(cache);
     if (st != PA_OK) return st;
     if (num_tokens < 0) return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PA_OK;  // nothing is touched, so empty tensors may pass null pointers
     if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PA_ERR_INVALID_ARG;
     if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(slot_mapping, 8))
         return PA_ERR_INVALID_ARG;
-    if (num_tokens == 0) return PA_OK;
     WriteArgs a{static_cast<const uint8_t*>(k_new),
                 static_cast<const uint8_t*>(v_new),
                 slot_mapping,
@@ -708,14 +708,14 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
                          size_t workspace_bytes, int32_t num_workers, pa_stream_t stream) {
     pa_status_t st = check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache);
     if (st != PA_OK) return st;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PA_OK;  // nothing is touched, so empty tensors may pass null pointers
     if (!q || !k_cache || !v_cache || !context_lens || !out) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(context_lens, 4) || (block_tables && !aligned(block_tables, 4)))
         return PA_ERR_INVALID_ARG;
-    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
-    if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
-    if (num_seqs == 0) return PA_OK;
     Plan plan;
     st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, &plan);
     if (st != PA_OK) return st;
