@@ -30,14 +30,18 @@
  *    values are clamped inside the kernels so they cannot fault, but the
  *    results are then unspecified.
  *
- * Cache layout (the same pool geometry for K and V; X = 16 / element bytes,
- * so X = 4 for f32 and 8 for f16/bf16):
- *    K pool: [num_blocks][num_kv_heads][head_dim / X][block_size][X]
- *    V pool: [num_blocks][num_kv_heads][head_dim][block_size]
- *  Token `o` of physical block `p`, kv-head `g`, dimension `d` is
- *    K[p][g][d / X][o][d % X]   and   V[p][g][d][o].
- *  One (block, kv-head) tile is block_size * head_dim contiguous elements in
- *  either pool.  A slot is p * block_size + o.
+ * Cache layout.  A block keeps its tokens in slabs of 16 consecutive tokens
+ * (block_size / 16 slabs per block).  Each (block, kv-head, slab) is
+ * 16 * head_dim contiguous elements; in either pool, the slab of token `o` of
+ * physical block `p`, kv-head `g` starts at element
+ *    ((p * num_kv_heads + g) * (block_size / 16) + o / 16) * 16 * head_dim.
+ * Inside a slab, with t = o % 16, X = 16 / element bytes (4 for f32, 8 for
+ * f16/bf16) and Y = 4 / element bytes (1 for f32, 2 for f16/bf16), dim `d` is
+ *    K: (d / X) * 16 * X + t * X + d % X
+ *    V: ((((d / (16*Y)) * 16 + d % 16) * 4 + t / 4) * Y + (d / 16) % Y) * 4 + t % 4
+ * (for f32 the V slab is simply the transpose, d * 16 + t).  This places each
+ * 16-byte piece that a matrix-core operand needs in one load, with
+ * consecutive lanes reading consecutive bytes.  A slot is p * block_size + o.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H

@@ -28,12 +28,14 @@
  *    arithmetic is double; stored values are widened exactly.
  *
  * Pool layout.  The pages fix none; this is the layout documented for the
- * library's caller.  With X = 16 / element_bytes,
- *    K pool: [num_blocks][Hkv][D / X][B][X]   (16-byte groups of a row, token-minor)
- *    V pool: [num_blocks][Hkv][D][B]          (a tile is V transposed)
- * so element (block p, kv-head g, offset o, dim d) sits at
- *    K: (((p*Hkv + g)*(D/X) + d/X)*B + o)*X + d%X
- *    V: ((p*Hkv + g)*D + d)*B + o
+ * library's caller.  A block keeps its tokens in slabs of 16 consecutive
+ * tokens (B a multiple of 16); each (block, kv-head, slab) holds 16 * D
+ * contiguous elements.  With X = 16 / element_bytes and Y = 4 / element_bytes,
+ * token t (0..15) and dim d of a slab sit at
+ *    K: (d / X) * 16 * X + t * X + d % X
+ *    V: ((((d / (16*Y)) * 16 + d % 16) * 4 + t / 4) * Y + (d / 16) % Y) * 4 + t % 4
+ * (for f32, Y = 1 and V is simply d * 16 + t: the slab transposed), and slab
+ * (p, g, o / 16) starts at element ((p * Hkv + g) * (B / 16) + o / 16) * 16 * D.
  */
 #include <math.h>
 #include <pthread.h>
@@ -74,21 +76,34 @@ static double widen(const void* base, size_t idx, int dtype) {
     return dtype == OR_F16 ? half_to_double(raw) : bf16_to_double(raw);
 }
 
-static size_t k_index(int64_t p, int g, int o, int d, int Hkv, int B, int D, int X) {
-    return ((((size_t)p * Hkv + g) * (size_t)(D / X) + (size_t)(d / X)) * (size_t)B + (size_t)o) * (size_t)X +
-           (size_t)(d % X);
+static size_t slab_base(int64_t p, int g, int o, int Hkv, int B, int D) {
+    return (((size_t)p * Hkv + g) * (size_t)(B / 16) + (size_t)(o / 16)) * 16 * (size_t)D;
 }
 
-static size_t v_index(int64_t p, int g, int o, int d, int Hkv, int B, int D) {
-    return (((size_t)p * Hkv + g) * (size_t)D + (size_t)d) * (size_t)B + (size_t)o;
+static size_t k_index(int64_t p, int g, int o, int d, int Hkv, int B, int D, int X) {
+    int t = o % 16;
+    return slab_base(p, g, o, Hkv, B, D) + (size_t)(d / X) * 16 * X + (size_t)t * X + (size_t)(d % X);
+}
+
+static size_t v_index(int64_t p, int g, int o, int d, int Hkv, int B, int D, int Y) {
+    int t = o % 16;
+    size_t in_slab = ((((size_t)(d / (16 * Y)) * 16 + (size_t)(d % 16)) * 4 + (size_t)(t / 4)) * Y +
+                      (size_t)((d / 16) % Y)) * 4 + (size_t)(t % 4);
+    return slab_base(p, g, o, Hkv, B, D) + in_slab;
+}
+
+/* Geometry the layout is defined for. */
+static int layout_ok(int B, int D, int dtype) {
+    int eb = elt_bytes(dtype);
+    return B > 0 && B % 16 == 0 && D > 0 && D % (16 * (4 / eb)) == 0;
 }
 
 /* Returns 0, or -1 on a bad argument. */
 int oracle_write_kv(const void* k_new, const void* v_new, const int64_t* slot, void* k_pool, void* v_pool,
                     int64_t num_tokens, int64_t num_blocks, int B, int Hkv, int D, int dtype) {
     int eb = elt_bytes(dtype);
-    int X = 16 / eb;
-    if (B <= 0 || Hkv <= 0 || D <= 0 || D % X) return -1;
+    int X = 16 / eb, Y = 4 / eb;
+    if (Hkv <= 0 || !layout_ok(B, D, dtype)) return -1;
     for (int64_t i = 0; i < num_tokens; ++i) {
         int64_t sl = slot[i];
         if (sl < 0) continue;
@@ -99,7 +114,7 @@ int oracle_write_kv(const void* k_new, const void* v_new, const int64_t* slot, v
             for (int d = 0; d < D; ++d) {
                 size_t src = ((size_t)i * Hkv + g) * (size_t)D + (size_t)d;
                 memcpy((char*)k_pool + k_index(p, g, o, d, Hkv, B, D, X) * eb, (const char*)k_new + src * eb, eb);
-                memcpy((char*)v_pool + v_index(p, g, o, d, Hkv, B, D) * eb, (const char*)v_new + src * eb, eb);
+                memcpy((char*)v_pool + v_index(p, g, o, d, Hkv, B, D, Y) * eb, (const char*)v_new + src * eb, eb);
             }
         }
     }
@@ -122,7 +137,7 @@ typedef struct {
 static int attend_one(const job_t* J, int s, int h, double* out_row) {
     int G = J->Hq / J->Hkv;
     int g = h / G;
-    int X = 16 / elt_bytes(J->dtype);
+    int X = 16 / elt_bytes(J->dtype), Y = 4 / elt_bytes(J->dtype);
     int L = J->ctx[s];
     int D = J->D;
     if (L < 0 || L > J->maxblk * J->B) return -1;
@@ -156,7 +171,7 @@ static int attend_one(const job_t* J, int s, int h, double* out_row) {
         den += w;
         int64_t p = J->bt[(size_t)s * J->maxblk + t / J->B];
         int o = t % J->B;
-        for (int d = 0; d < D; ++d) out_row[d] += w * widen(J->v_pool, v_index(p, g, o, d, J->Hkv, J->B, D), J->dtype);
+        for (int d = 0; d < D; ++d) out_row[d] += w * widen(J->v_pool, v_index(p, g, o, d, J->Hkv, J->B, D, Y), J->dtype);
     }
     for (int d = 0; d < D; ++d) out_row[d] /= den;
     free(q);
@@ -192,7 +207,7 @@ static void* run_job(void* arg) {
 int oracle_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
                   const int32_t* context_lens, float scale, double* out, int S, int Hq, int Hkv, int D, int B,
                   int max_blocks_per_seq, int dtype, const int32_t* pairs, int64_t npairs, int nthreads) {
-    if (Hkv <= 0 || Hq % Hkv || D <= 0 || B <= 0 || D % (16 / elt_bytes(dtype))) return -1;
+    if (Hkv <= 0 || Hq % Hkv || !layout_ok(B, D, dtype)) return -1;
     int64_t n = pairs ? npairs : (int64_t)S * Hq;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > n) nthreads = n > 0 ? (int)n : 1;

@@ -12,7 +12,9 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+# PAGEDATTN_LIB selects another build of the library (for example a differently tuned one).
+_LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                           "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
@@ -88,10 +90,15 @@ def _check(fn: str, status: int) -> None:
 
 
 def cache_shapes(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype):
-    """Shapes of the K and V pools in the library's layout."""
-    X = 16 // _ELT[dtype]
-    return ((num_blocks, num_kv_heads, head_dim // X, block_size, X),
-            (num_blocks, num_kv_heads, head_dim, block_size))
+    """Shapes of the K and V pools: [num_blocks, Hkv, block_size/16, 16*head_dim] each.
+
+    The last dimension is one 16-token slab; the element order inside a slab is
+    the library's (see include/pagedattn.h).
+    """
+    if block_size % 16:
+        raise ValueError("block_size must be a multiple of 16")
+    shape = (num_blocks, num_kv_heads, block_size // 16, 16 * head_dim)
+    return shape, shape
 
 
 def new_cache(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
@@ -102,20 +109,17 @@ def new_cache(num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int
 
 
 def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> CacheDesc:
-    """The pool geometry, read from the pools' shapes (which must match the layout)."""
-    if k_cache.dim() != 5 or v_cache.dim() != 4:
-        raise ValueError("k_cache must be [NB, Hkv, D/X, B, X] and v_cache [NB, Hkv, D, B]")
-    NB, Hkv, DX, B, X = k_cache.shape
+    """The pool geometry, read from the pools' shapes [NB, Hkv, B/16, 16*D]."""
+    if k_cache.dim() != 4 or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must both be [num_blocks, Hkv, block_size/16, 16*head_dim]")
     if k_cache.dtype not in _DTYPE_CODE or v_cache.dtype != k_cache.dtype:
         raise ValueError("caches must share one of float32/float16/bfloat16")
-    if X * _ELT[k_cache.dtype] != 16:
-        raise ValueError("innermost K dimension must hold 16 bytes")
-    D = DX * X
-    if tuple(v_cache.shape) != (NB, Hkv, D, B):
-        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} does not match k_cache {tuple(k_cache.shape)}")
+    NB, Hkv, NS, SL = k_cache.shape
+    if SL % 16:
+        raise ValueError("the last dimension must be 16 * head_dim")
     if not (k_cache.is_contiguous() and v_cache.is_contiguous()):
         raise ValueError("caches must be contiguous")
-    return CacheDesc(NB, B, Hkv, D, _DTYPE_CODE[k_cache.dtype])
+    return CacheDesc(NB, NS * 16, Hkv, SL // 16, _DTYPE_CODE[k_cache.dtype])
 
 
 def _stream(device: torch.device) -> ctypes.c_void_p:

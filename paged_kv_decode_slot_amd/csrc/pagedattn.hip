@@ -16,10 +16,10 @@
 //    dealt to the workers in equal contiguous runs ("stream-K"), so every
 //    worker streams the same number of blocks whatever the length mix.  A
 //    run that covers a whole (sequence, kv-head) writes the output directly;
-//    one that covers part of it writes (o, log-sum-exp) and a merge kernel
-//    combines the parts.  The split depends only on the lengths and the
-//    worker count, so results are bitwise reproducible and independent of
-//    physical placement.
+//    one that covers part of it stores (o, log-sum-exp), and the wave that
+//    stores the last part of a pair merges the parts, inside the same launch.
+//    The split depends only on the lengths and the worker count, so results
+//    are bitwise reproducible and independent of physical placement.
 //  * Per 16-token tile, the G query heads of a kv-head form the columns of
 //    one 16x16 MFMA tile: S = K * Q^T (tokens x heads), then O^T += V^T * P^T
 //    (dims x heads).  P comes out of the first product in exactly the lane
@@ -42,12 +42,19 @@
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerGroup = 4;
+#ifndef PA_WAVES_PER_GROUP
+#define PA_WAVES_PER_GROUP 2
+#endif
+constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;
 constexpr int kGroupThreads = kWave * kWavesPerGroup;
+constexpr int kWriteThreads = 256;
 constexpr int kMaxSeqs = 4096;
 constexpr int kMaxGroup = 16;
-constexpr int kWorkersPerCU = 8;
-constexpr int kMinBlocksPerWorker = 4;
+#ifndef PA_WORKERS_PER_CU
+#define PA_WORKERS_PER_CU 2
+#endif
+constexpr int kWorkersPerCU = PA_WORKERS_PER_CU;
+constexpr int kMinBlocksPerWorker = 16;
 constexpr int kMaxWorkers = 1 << 20;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -65,20 +72,12 @@ struct Cfg {
     static constexpr int kElt = DT == PA_F32 ? 4 : 2;
     static constexpr int kKFrag = D * kElt / 64;  // 16-byte K pieces per lane per 16-token tile
     static constexpr int kVChunk = D / 16;        // 16-dim chunks of the output
+    static constexpr int kVPiece = D * kElt / 64;  // 16-byte V pieces per lane per tile (4/kElt chunks each)
     static constexpr int kSub = B / 16;           // 16-token tiles per block
     static constexpr int kTileBytes = B * D * kElt;
+    static constexpr int kSlabBytes = 16 * D * kElt;  // one 16-token slab of a tile
 };
 
-template <int ELT>
-struct VPiece;  // the V bytes one lane feeds to one PV product: 4 tokens
-template <>
-struct VPiece<2> {
-    using type = uint2;
-};
-template <>
-struct VPiece<4> {
-    using type = uint4;
-};
 
 // ---------------------------------------------------------------- MFMA steps
 
@@ -130,33 +129,36 @@ __device__ inline PPack<DT> pack_p(const float p[4]) {
     return r;
 }
 
-// O^T (16 dims x 16 heads) += V^T piece (16 dims x 4k tokens) x P^T.
+// O^T (16 dims x 16 heads) += V^T (16 dims x 4 tokens per lane group) x P^T, for
+// the chunks in one 16-byte V piece: two 16-dim chunks (halves .xy, .zw) for
+// 16-bit types, one (all of it) for f32.
 template <int DT>
-__device__ inline f32x4 pv_step(typename VPiece<DT == PA_F32 ? 4 : 2>::type v, PPack<DT> p, f32x4 acc) {
+__device__ inline void pv_piece(uint4 v, PPack<DT> p, f32x4* O) {
     if constexpr (DT == PA_BF16) {
-        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, v), p.v, acc, 0, 0, 0);
+        O[0] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, make_uint2(v.x, v.y)), p.v, O[0], 0, 0, 0);
+        O[1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, make_uint2(v.z, v.w)), p.v, O[1], 0, 0, 0);
     } else if constexpr (DT == PA_F16) {
-        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v), p.v, acc, 0, 0, 0);
+        O[0] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, make_uint2(v.x, v.y)), p.v, O[0], 0, 0, 0);
+        O[1] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, make_uint2(v.z, v.w)), p.v, O[1], 0, 0, 0);
     } else {
         f32x4 vf = __builtin_bit_cast(f32x4, v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e], p.v[e], acc, 0, 0, 0);
-        return acc;
+        for (int e = 0; e < 4; ++e) O[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[e], p.v[e], O[0], 0, 0, 0);
     }
 }
 
 // Zero the V entries of tokens at or past the context end (their P is 0, but
-// 0 * NaN would still poison the sum).
+// 0 * NaN would still poison the sum).  Token first_tok + e is element e of
+// each 4-token group in the piece.
 template <int ELT>
-__device__ inline void mask_v(typename VPiece<ELT>::type& v, int first_tok, int ctx) {
+__device__ inline void mask_v(uint4& v, int first_tok, int ctx) {
     if constexpr (ELT == 2) {
-        uint32_t lo = v.x, hi = v.y;
-        if (first_tok + 0 >= ctx) lo &= 0xffff0000u;
-        if (first_tok + 1 >= ctx) lo &= 0x0000ffffu;
-        if (first_tok + 2 >= ctx) hi &= 0xffff0000u;
-        if (first_tok + 3 >= ctx) hi &= 0x0000ffffu;
-        v.x = lo;
-        v.y = hi;
+        const uint32_t m01 = (first_tok + 0 >= ctx ? 0u : 0x0000ffffu) | (first_tok + 1 >= ctx ? 0u : 0xffff0000u);
+        const uint32_t m23 = (first_tok + 2 >= ctx ? 0u : 0x0000ffffu) | (first_tok + 3 >= ctx ? 0u : 0xffff0000u);
+        v.x &= m01;
+        v.z &= m01;
+        v.y &= m23;
+        v.w &= m23;
     } else {
         if (first_tok + 0 >= ctx) v.x = 0;
         if (first_tok + 1 >= ctx) v.y = 0;
@@ -179,6 +181,22 @@ __device__ inline void store4(uint8_t* dst, f32x4 x) {
     }
 }
 
+// Store 2 consecutive fp32 values as the storage type (round to nearest even).
+template <int DT>
+__device__ inline void store2(uint8_t* dst, float2 x) {
+    if constexpr (DT == PA_BF16) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        bf16x2 b = {(__bf16)x.x, (__bf16)x.y};
+        *reinterpret_cast<uint32_t*>(dst) = __builtin_bit_cast(uint32_t, b);
+    } else if constexpr (DT == PA_F16) {
+        typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+        f16x2 h = {(_Float16)x.x, (_Float16)x.y};
+        *reinterpret_cast<uint32_t*>(dst) = __builtin_bit_cast(uint32_t, h);
+    } else {
+        *reinterpret_cast<float2*>(dst) = x;
+    }
+}
+
 // ---------------------------------------------------------------- arguments
 
 struct DecodeArgs {
@@ -188,10 +206,11 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     uint8_t* out;
-    int32_t* seq_prefix;  // [num_seqs + 1] blocks before each sequence, or null
-    float* part_lse;      // [workers][2][G]
-    float* part_o;        // [workers][2][G][D]
+    unsigned long long* arrivals;  // [num_seqs * Hkv]: (call tag << 32) | parts stored so far
+    float* part_lse;               // [workers][2][G]
+    float* part_o;                 // [workers][2][G][D]
     float scale_log2;
+    uint32_t tag;  // nonzero; differs between consecutive calls
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -202,26 +221,25 @@ struct DecodeArgs {
     int32_t per_segment;  // 1: worker w owns (sequence, kv-head) w entirely
 };
 
-__device__ inline int blocks_of(int ctx, int B, int max_blocks) {
-    ctx = ctx < 0 ? 0 : ctx;
-    int nb = (ctx + B - 1) / B;
-    return nb > max_blocks ? max_blocks : nb;
-}
-
 __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
     ctx = ctx < 0 ? 0 : ctx;
     return ctx > max_blocks * B ? max_blocks * B : ctx;
 }
 
-// Exclusive prefix over sequences of their block counts, into LDS [num_seqs + 1].
+// Context lengths (clamped) and the exclusive prefix over sequences of their
+// block counts, into LDS: ctx[S], pre[S + 1].
 template <int B>
-__device__ void build_prefix(const DecodeArgs& a, int32_t* pre, int32_t* wave_tot) {
+__device__ void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, int32_t* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = a.num_seqs;
     const int per = (S + kGroupThreads - 1) / kGroupThreads;
     const int lo = min(S, tid * per), hi = min(S, lo + per);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += blocks_of(a.context_lens[i], B, a.max_blocks);
+    for (int i = lo; i < hi; ++i) {
+        const int c = clamp_ctx(a.context_lens[i], B, a.max_blocks);
+        ctx[i] = c;
+        sum += (c + B - 1) / B;
+    }
     int x = sum;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -234,7 +252,7 @@ __device__ void build_prefix(const DecodeArgs& a, int32_t* pre, int32_t* wave_to
     for (int w = 0; w < wave; ++w) run += wave_tot[w];
     for (int i = lo; i < hi; ++i) {
         pre[i] = run;
-        run += blocks_of(a.context_lens[i], B, a.max_blocks);
+        run += (ctx[i] + B - 1) / B;
     }
     if (tid == kGroupThreads - 1) pre[S] = run;
     __syncthreads();
@@ -253,26 +271,258 @@ __device__ inline int find_seq(const int32_t* pre, int S, int v) {
     return lo;
 }
 
+// Runs: worker w streams units [w*U/W, (w+1)*U/W).
+__device__ inline int64_t run_start(int64_t w, int64_t U, int64_t W) { return w * U / W; }
+
+// The worker whose run holds unit u.
+__device__ inline int64_t owner_of(int64_t u, int64_t U, int64_t W) { return ((u + 1) * W + U - 1) / U - 1; }
+
+// Partial results cross workgroups (and the XCDs' separate L2 caches) inside
+// one launch.  They are written and read only with device-coherent accesses
+// (relaxed agent-scope atomics: they go to, and come from, the device's
+// coherence point rather than a possibly stale XCD-local L2 line), so a writer
+// needs only to wait for its stores to complete before it counts its part,
+// and the last wave reads the parts after its count returns.  This is what an
+// agent-scope release/acquire pair amounts to when every shared access is
+// itself coherent, without writing back and invalidating whole L2 caches.
+__device__ inline void coherent_store(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float coherent_load(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// All of this wave's outstanding vector-memory operations (stores included) complete.
+__device__ inline void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Count this wave's part of a split (sequence, kv-head); true for the wave
+// that stores the last part.  The word holds (tag << 32) | parts counted; a
+// word carrying another call's tag (an earlier call, or uninitialised memory)
+// is first claimed for this call by a compare-exchange that also counts this
+// part; every other part is one fetch-add, so simultaneous arrivals never
+// retry each other.  The last part clears the word (tag 0 is never used), so a
+// replay of the same call starts from zero again.  A failed claim means
+// another wave changed the word, so the loop ends after a few rounds.
+__device__ inline bool arrive(unsigned long long* word, uint32_t tag, int parts) {
+    const unsigned long long mine = (unsigned long long)tag << 32;
+    unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while ((old >> 32) != tag) {
+        const unsigned long long prev = atomicCAS(word, old, mine | 1ull);
+        if (prev == old) return parts == 1;
+        old = prev;
+    }
+    const unsigned long long prev = atomicAdd(word, 1ull);
+    if ((int)(prev & 0xffffffffull) + 1 != parts) return false;
+    atomicExch(word, 0ull);
+    return true;
+}
+
 // ---------------------------------------------------------------- decode: one run of blocks
+
+// A pointer through which uniform loads become scalar-memory loads.
+typedef const int32_t __attribute__((address_space(4)))* ScalarPtr;
+
+
+#ifndef PA_TILE_BUFFERS
+#define PA_TILE_BUFFERS 2  // 16-token tiles in registers: one being consumed, the rest in flight
+#endif
+#ifndef PA_KV_NONTEMPORAL
+#define PA_KV_NONTEMPORAL 1  // K/V are read once: hint the caches not to keep them
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+__device__ inline T load_kv(const uint8_t* p) {
+#if PA_KV_NONTEMPORAL
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+#else
+    return *reinterpret_cast<const T*>(p);
+#endif
+}
 
 template <int DT, int D, int B>
 struct Tile {
     uint4 k[Cfg<DT, D, B>::kKFrag];
-    typename VPiece<Cfg<DT, D, B>::kElt>::type v[Cfg<DT, D, B>::kVChunk];
+    uint4 v[Cfg<DT, D, B>::kVPiece];
 };
 
-// Attend query group (s, kvh) over logical blocks [j0, j1) of sequence s.
-// whole: the run is the sequence's entire context (write out), otherwise
-// write a partial into slot `slot` of worker `w`.
+// Where a worker's partial result for one split (sequence, kv-head) lives.
+__device__ inline size_t part_index(int64_t w, int slot, int G, int h) { return ((size_t)w * 2 + slot) * G + h; }
+
+// Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48:
+// one head's four row groups).  permlane16/32_swap leave, in the two halves of
+// their result, a lane's own value and that of its partner 16 (32) lanes away,
+// in some order; both are plain VALU operations.
+__device__ inline float row_group_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float row_group_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Per-wave LDS used by a merge: part weights and locations of up to 64 parts,
+// per-head running maximum, denominator and rescale factor, and the output
+// accumulators (pass p holds head p*HP + lane/LH, dims 2*(lane%LH) + {0,1}).
+struct MergeLds {
+    float w[kWave][kMaxGroup];  // weight of part k for head h (relative to the running max)
+    int32_t loc[kWave];         // part_index(worker, slot, G, 0) of part k
+    float M[kMaxGroup];         // running maximum of the parts' log-sum-exps (log2 domain)
+    float den[kMaxGroup];       // running sum of weights
+    float rescale[kMaxGroup];   // factor applied to earlier chunks when the running max grows
+    float2 acc[kMaxGroup][kWave];
+};
+
+// Lane x of the same 16-lane row, by DPP: quad_perm [1,0,3,2] (xor 1),
+// quad_perm [2,3,0,1] (xor 2), row_ror 4 and row_ror 8.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// Whole-wave reductions without LDS: all-reduce within each 16-lane row by DPP,
+// then across the four rows with the permlane swaps.
+__device__ inline float wave_max(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x124>(x));
+    x = fmaxf(x, dpp<0x128>(x));
+    return row_group_max(x);
+}
+__device__ inline float wave_sum(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x124>(x);
+    x += dpp<0x128>(x);
+    return row_group_sum(x);
+}
+__device__ inline float2 coherent_load2(const float* p) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_bit_cast(float2, v);
+}
+
+// Combine the parts of a split (sequence, kv-head) by log-sum-exp and write out.
+// Parts are the workers whose runs cover units [F, F + nb): with W >= U each
+// unit is its own run; otherwise they are owner(F) .. owner(F + nb - 1), all
+// in slot 0 except the first when its run began in an earlier pair.
+// Parts are taken 64 at a time: lanes read the 64 parts' log-sum-exps at once
+// (the maximum and the weights follow by wave reductions); then the (pass,
+// part) items of the chunk are read kBatch at a time, each lane loading two
+// output dims of one head per item, and accumulated in LDS.
+template <int DT, int D>
+__device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int64_t F, int nb, int64_t U, int64_t W,
+                            MergeLds& L) {
+    constexpr int E = DT == PA_F32 ? 4 : 2;
+    constexpr int LH = D / 2;       // lanes per head: one pair of dims each
+    constexpr int HP = kWave / LH;  // heads per pass over the lanes
+    constexpr int kBatch = 32;      // item loads in flight per lane
+    const int lane = threadIdx.x & 63, G = a.group;
+    const bool unit_runs = W >= U;
+    const int64_t wa = owner_of(F, U, W);
+    const int parts = unit_runs ? nb : (int)(owner_of(F + nb - 1, U, W) - wa + 1);
+    const int first_slot = run_start(wa, U, W) == F ? 0 : 1;
+    const int pl = lane % LH, hs = lane / LH;
+    const int passes = (G + HP - 1) / HP;
+
+    if (lane < kMaxGroup) {
+        L.M[lane] = -INFINITY;
+        L.den[lane] = 0.f;
+    }
+    for (int p = 0; p < passes; ++p) L.acc[p][lane] = float2{0.f, 0.f};
+    __builtin_amdgcn_wave_barrier();
+
+    for (int k0 = 0; k0 < parts; k0 += kWave) {
+        const int cnt = min(kWave, parts - k0);
+        // Phase 1: lane k reads part k0 + k's log-sum-exps.
+        const int k = k0 + lane;
+        const bool has = lane < cnt;
+        const int64_t wk = !has ? 0 : (unit_runs ? owner_of(F + k, U, W) : wa + k);
+        const int loc = has ? (int)part_index(wk, k == 0 ? first_slot : 0, G, 0) : 0;
+        float l[kMaxGroup];
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) l[h] = (has && h < G) ? coherent_load(a.part_lse + loc + h) : -INFINITY;
+        L.loc[lane] = loc;
+        for (int h = 0; h < G; ++h) {
+            float lh = l[0];
+#pragma unroll
+            for (int i = 1; i < kMaxGroup; ++i)
+                if (i == h) lh = l[i];
+            const float m_old = L.M[h];
+            const float mn = fmaxf(m_old, wave_max(lh));
+            const float sc = __builtin_amdgcn_exp2f(m_old - mn);  // 0 while m_old is -inf
+            const float wt = has ? __builtin_amdgcn_exp2f(lh - mn) : 0.f;
+            const float dn = L.den[h] * sc + wave_sum(wt);
+            L.w[lane][h] = wt;
+            __builtin_amdgcn_wave_barrier();
+            if (lane == 0) {
+                L.M[h] = mn;
+                L.den[h] = dn;
+                L.rescale[h] = sc;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+        // Phase 2: item (p, kk) adds part kk's dims 2pl, 2pl+1 of head p*HP + hs.
+        for (int p = 0; p < passes; ++p) L.acc[p][lane] *= L.rescale[min(p * HP + hs, G - 1)];
+        const int items = passes * cnt;
+        for (int i0 = 0; i0 < items; i0 += kBatch) {
+            float2 v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int it = i0 + b;
+                if (it < items) {
+                    const int p = it / cnt, kk = it - p * cnt;
+                    const int hh = min(p * HP + hs, G - 1);
+                    v[b] = coherent_load2(a.part_o + ((size_t)L.loc[kk] + hh) * D + 2 * pl);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int it = i0 + b;
+                if (it < items) {
+                    const int p = it / cnt, kk = it - p * cnt;
+                    const int hh = min(p * HP + hs, G - 1);
+                    L.acc[p][lane] += L.w[kk][hh] * v[b];
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    for (int p = 0; p < passes; ++p) {
+        const int h = p * HP + hs;
+        if (h < G) {
+            uint8_t* dst = a.out + (((size_t)s * a.num_q_heads + kvh * G + h) * D + 2 * pl) * E;
+            store2<DT>(dst, L.acc[p][lane] * (1.f / L.den[h]));
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Attend query group (s, kvh) over logical blocks [j0, j1) of sequence s, whose
+// pair (s, kvh) occupies units [F, F + nb).  A run over the whole context
+// writes out; otherwise the run stores a partial in slot `slot` of worker w,
+// and the wave that stores the pair's last partial merges them.
 template <int DT, int D, int B>
-__device__ void attend_run(const DecodeArgs& a, int s, int kvh, int j0, int j1, bool whole, int w, int slot) {
+__device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0, int j1, int nb, int64_t F,
+                           int64_t U, int64_t W, int w, int slot, MergeLds& mlds) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
+    constexpr int NBUF = PA_TILE_BUFFERS;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;  // this lane's head column (and row within a 16-row piece)
     const int r = lane >> 4;  // this lane's group of 4 rows / k-range
     const int G = a.group;
-    const int ctx = __builtin_amdgcn_readfirstlane(clamp_ctx(a.context_lens[s], B, a.max_blocks));
+
+    // Block ids are read with scalar loads (the row of the table is the same for
+    // the whole wave), one block ahead, so waiting for one never waits on the
+    // K/V loads in flight.
+    const ScalarPtr bt = (ScalarPtr)(a.block_tables + (size_t)s * a.max_blocks);
+    int next_id = bt[j0];
 
     // Q of the lane's head, in the B-operand form of the QK product.
     uint4 qf[C::kKFrag];
@@ -292,36 +542,39 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int j0, int j1, 
     float m = -INFINITY;  // running max (log2 domain) of this lane's head
     float lsum = 0.f;     // this lane's share of the running denominator
 
-    const int32_t* bt = a.block_tables + (size_t)s * a.max_blocks;
     const size_t blk_stride = (size_t)a.num_kv_heads * C::kTileBytes;
     const size_t head_off = (size_t)kvh * C::kTileBytes;
     const int ntiles = (j1 - j0) * C::kSub;
 
-    int id_base = j0;
-    int ids = (j0 + lane < j1) ? bt[j0 + lane] : 0;
-
+    int phys = 0;
     auto issue = [&](int tau, Tile<DT, D, B>& t) {
         const int j = j0 + tau / C::kSub, u = tau % C::kSub;
-        if (j - id_base >= kWave) {
-            id_base += kWave;
-            ids = (id_base + lane < j1) ? bt[id_base + lane] : 0;
+        if (u == 0) {  // first tile of block j: take its id, fetch the next one
+            phys = ((unsigned)next_id < (unsigned)a.num_blocks) ? next_id : 0;
+            if (j + 1 < j1) next_id = bt[j + 1];
         }
-        int phys = __builtin_amdgcn_readlane(ids, j - id_base);
-        phys = ((unsigned)phys < (unsigned)a.num_blocks) ? phys : 0;
-        const uint8_t* kt = a.k_cache + (size_t)phys * blk_stride + head_off;
-        const uint8_t* vt = a.v_cache + (size_t)phys * blk_stride + head_off;
+        // The 16-token slab u of this (block, kv-head) tile: 16 * D contiguous elements.
+        const size_t slab = (size_t)phys * blk_stride + head_off + (size_t)u * C::kSlabBytes;
+        const uint8_t* kt = a.k_cache + slab;
+        const uint8_t* vt = a.v_cache + slab;
 #pragma unroll
         for (int f = 0; f < C::kKFrag; ++f)
-            t.k[f] = *reinterpret_cast<const uint4*>(kt + ((4 * f + r) * B + 16 * u + n) * 16);
+            t.k[f] = __builtin_bit_cast(uint4, load_kv<u32x4>(kt + ((4 * f + r) * 16 + n) * 16));
 #pragma unroll
-        for (int c = 0; c < C::kVChunk; ++c)
-            t.v[c] = *reinterpret_cast<const typename VPiece<E>::type*>(vt + ((16 * c + n) * B + 16 * u + 4 * r) * E);
+        for (int c = 0; c < C::kVPiece; ++c)
+            t.v[c] = __builtin_bit_cast(uint4, load_kv<u32x4>(vt + ((c * 16 + n) * 4 + r) * 16));
     };
 
-    auto consume = [&](int tau, Tile<DT, D, B>& t) {
+    // m is a reference maximum, not necessarily the running one: weights are
+    // exp2(z - m), and m (with O and lsum) is moved up only when some head's
+    // tile maximum exceeds it by more than kLazy, so most tiles skip the
+    // rescale.  Weights then stay below 2^kLazy, far inside fp32 and the
+    // 16-bit P operand's range, and O / lsum is unchanged by the choice of m.
+    constexpr float kLazy = 8.f;
+    auto consume = [&](int tau, Tile<DT, D, B>& t, bool may_be_partial) {
         const int j = j0 + tau / C::kSub, u = tau % C::kSub;
         const int tok0 = j * B + 16 * u + 4 * r;  // position of this lane's first row
-        const bool partial = j * B + 16 * u + 16 > ctx;
+        const bool partial = may_be_partial && j * B + 16 * u + 16 > ctx;
 
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -333,68 +586,114 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int j0, int j1, 
             z[e] = sc[e] * a.scale_log2;
             if (partial && tok0 + e >= ctx) z[e] = -INFINITY;
         }
-        float tmax = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float m_new = fmaxf(m, tmax);
-        const float alpha = (m == m_new) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+        const float tmax = row_group_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+        if (__builtin_amdgcn_read_exec() & __ballot(tmax > m + kLazy)) {
+            const float m_new = fmaxf(m, tmax);
+            const float alpha = (m == m_new) ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+            lsum *= alpha;
+#pragma unroll
+            for (int c = 0; c < C::kVChunk; ++c) O[c] *= alpha;
+            m = m_new;
+        }
         float p[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = (z[e] > -INFINITY) ? __builtin_amdgcn_exp2f(z[e] - m_new) : 0.f;
-        lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-        m = m_new;
-#pragma unroll
-        for (int c = 0; c < C::kVChunk; ++c) O[c] *= alpha;
+        for (int e = 0; e < 4; ++e) p[e] = (z[e] > -INFINITY) ? __builtin_amdgcn_exp2f(z[e] - m) : 0.f;
+        lsum += (p[0] + p[1]) + (p[2] + p[3]);
 
         if (partial) {
 #pragma unroll
-            for (int c = 0; c < C::kVChunk; ++c) mask_v<E>(t.v[c], tok0, ctx);
+            for (int c = 0; c < C::kVPiece; ++c) mask_v<E>(t.v[c], tok0, ctx);
         }
         const PPack<DT> pp = pack_p<DT>(p);
 #pragma unroll
-        for (int c = 0; c < C::kVChunk; ++c) O[c] = pv_step<DT>(t.v[c], pp, O[c]);
+        for (int c = 0; c < C::kVPiece; ++c) pv_piece<DT>(t.v[c], pp, &O[c * (4 / E)]);
     };
 
-    Tile<DT, D, B> t0, t1;
-    issue(0, t0);
-    for (int tau = 0; tau < ntiles; tau += 2) {
-        if (tau + 1 < ntiles) issue(tau + 1, t1);
-        consume(tau, t0);
-        if (tau + 1 < ntiles) {
-            if (tau + 2 < ntiles) issue(tau + 2, t0);
-            consume(tau + 1, t1);
+    // Ring of NBUF tiles: tile tau lives in buf[tau % NBUF]; NBUF - 1 tiles are
+    // in flight while one is consumed.  The steady-state loop issues exactly one
+    // tile per step on every path, so the wait before consuming a tile counts
+    // only the loads issued after it and never drains the ring; the first and
+    // last steps are peeled.
+    // Only the last kSub tiles of a sequence can reach past its end; the
+    // steady loop stops early enough that those always fall in the peeled
+    // tail, so it never pays for masking.
+    constexpr int kTail = (NBUF - 1 > C::kSub ? NBUF - 1 : C::kSub);
+    Tile<DT, D, B> buf[NBUF];
+    if (ntiles < NBUF) {
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i)
+            if (i < ntiles) issue(i, buf[i]);
+#pragma unroll
+        for (int i = 0; i < NBUF; ++i)
+            if (i < ntiles) consume(i, buf[i], true);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; ++i) issue(i, buf[i]);
+        int tau0 = 0;
+        for (; tau0 + NBUF - 1 + kTail < ntiles; tau0 += NBUF) {
+#pragma unroll
+            for (int k = 0; k < NBUF; ++k) {
+                issue(tau0 + k + NBUF - 1, buf[(k + NBUF - 1) % NBUF]);
+                consume(tau0 + k, buf[k], false);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NBUF + kTail; ++k) {
+            const int tau = tau0 + k;
+            if (tau < ntiles) {
+                if (tau + NBUF - 1 < ntiles) issue(tau + NBUF - 1, buf[(k + NBUF - 1) % NBUF]);
+                consume(tau, buf[k % NBUF], true);
+            }
         }
     }
 
     // Full denominator of the lane's head: the four row groups hold disjoint tokens.
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
-    if (n >= G) return;
+    lsum = row_group_sum(lsum);
     const float inv = 1.f / lsum;
-    if (whole) {
-        uint8_t* orow = a.out + ((size_t)s * a.num_q_heads + kvh * G + n) * (size_t)(D * E);
+    if (j0 == 0 && j1 == nb) {
+        if (n < G) {
+            uint8_t* orow = a.out + ((size_t)s * a.num_q_heads + kvh * G + n) * (size_t)(D * E);
 #pragma unroll
-        for (int c = 0; c < C::kVChunk; ++c) store4<DT>(orow + (16 * c + 4 * r) * E, O[c] * inv);
-    } else {
-        const size_t part = ((size_t)w * 2 + slot) * G + n;
+            for (int c = 0; c < C::kVChunk; ++c) store4<DT>(orow + (16 * c + 4 * r) * E, O[c] * inv);
+        }
+        return;
+    }
+    if (n < G) {
+        const size_t part = part_index(w, slot, G, n);
         float* po = a.part_o + part * D;
 #pragma unroll
-        for (int c = 0; c < C::kVChunk; ++c) *reinterpret_cast<f32x4*>(po + 16 * c + 4 * r) = O[c] * inv;
-        if (r == 0) a.part_lse[part] = m + __log2f(lsum);
+        for (int c = 0; c < C::kVChunk; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) coherent_store(po + 16 * c + 4 * r + e, O[c][e] * inv);
+        if (r == 0) coherent_store(a.part_lse + part, m + __log2f(lsum));
     }
+    // Publish the partial (wait until its device-coherent stores are done),
+    // then count it; the wave that stores the last part merges.
+    wait_stores_done();
+    const int parts = W >= U ? nb : (int)(owner_of(F + nb - 1, U, W) - owner_of(F, U, W) + 1);
+    int last = 0;
+    if (lane == 0) last = arrive(a.arrivals + (size_t)s * a.num_kv_heads + kvh, a.tag, parts) ? 1 : 0;
+    if (__shfl(last, 0)) merge_parts<DT, D>(a, s, kvh, F, nb, U, W, mlds);
 }
 
+constexpr size_t kDecodeStaticLds = sizeof(MergeLds) * kWavesPerGroup + sizeof(int32_t) * kWavesPerGroup;
+
+#ifndef PA_MIN_WAVES_PER_SIMD
+#define PA_MIN_WAVES_PER_SIMD 1
+#endif
+
 template <int DT, int D, int B>
-__global__ __launch_bounds__(kGroupThreads) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
     using C = Cfg<DT, D, B>;
-    extern __shared__ int32_t s_prefix[];  // [num_seqs + 1]
+    extern __shared__ int32_t s_lds[];  // ctx[num_seqs], pre[num_seqs + 1]
     __shared__ int32_t s_wave_tot[kWavesPerGroup];
-    build_prefix<B>(a, s_prefix, s_wave_tot);
-    if (blockIdx.x == 0 && a.seq_prefix != nullptr)
-        for (int i = threadIdx.x; i <= a.num_seqs; i += kGroupThreads) a.seq_prefix[i] = s_prefix[i];
+    __shared__ MergeLds s_merge[kWavesPerGroup];
+    int32_t* s_ctx = s_lds;
+    int32_t* s_pre = s_lds + a.num_seqs;
+    load_lengths<B>(a, s_ctx, s_pre, s_wave_tot);
 
     const int lane = threadIdx.x & 63;
-    const int w = blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
     if (w >= a.num_workers) return;
     const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
     const int W = a.num_workers;
@@ -402,19 +701,19 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(DecodeArgs a) {
     // Sequences with no context get out = 0; worker w takes the pairs z = w (mod W).
     for (int z = w; z < S * Hkv; z += W) {
         const int s = z / Hkv, kvh = z % Hkv;
-        if (s_prefix[s + 1] != s_prefix[s]) continue;
+        if (s_ctx[s] != 0) continue;
         uint8_t* orow = a.out + ((size_t)s * a.num_q_heads + (size_t)kvh * G) * (size_t)(D * C::kElt);
         for (int i = lane; i < G * D * C::kElt / 16; i += kWave)
             reinterpret_cast<uint4*>(orow)[i] = make_uint4(0, 0, 0, 0);
     }
 
-    const int64_t U = (int64_t)s_prefix[S] * Hkv;
+    const int64_t U = (int64_t)s_pre[S] * Hkv;
     int64_t start, end;
     if (a.per_segment) {
         if (w >= S * Hkv) return;
         const int s = w / Hkv, kvh = w % Hkv;
-        const int nb = s_prefix[s + 1] - s_prefix[s];
-        start = (int64_t)s_prefix[s] * Hkv + (int64_t)kvh * nb;
+        const int nb = s_pre[s + 1] - s_pre[s];
+        start = (int64_t)s_pre[s] * Hkv + (int64_t)kvh * nb;
         end = start + nb;
     } else {
         start = (int64_t)w * U / W;
@@ -422,72 +721,17 @@ __global__ __launch_bounds__(kGroupThreads) void decode_kernel(DecodeArgs a) {
     }
     for (int64_t u = start; u < end;) {
         // Every lane holds the same values; readfirstlane lets them live in scalar registers.
-        const int s = __builtin_amdgcn_readfirstlane(find_seq(s_prefix, S, (int)(u / Hkv)));
-        const int base = __builtin_amdgcn_readfirstlane(s_prefix[s]);
-        const int nb = __builtin_amdgcn_readfirstlane(s_prefix[s + 1]) - base;
+        const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, (int)(u / Hkv)));
+        const int base = __builtin_amdgcn_readfirstlane(s_pre[s]);
+        const int nb = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - base;
+        const int ctx = __builtin_amdgcn_readfirstlane(s_ctx[s]);
         const int off = (int)(u - (int64_t)base * Hkv);
         const int kvh = off / nb, j0 = off % nb;
         const int64_t left = end - u;
         const int j1 = left < (int64_t)(nb - j0) ? j0 + (int)left : nb;
-        attend_run<DT, D, B>(a, s, kvh, j0, j1, j0 == 0 && j1 == nb, w, u == start ? 0 : 1);
+        const int64_t F = (int64_t)base * Hkv + (int64_t)kvh * nb;
+        attend_run<DT, D, B>(a, s, kvh, ctx, j0, j1, nb, F, U, W, w, u == start ? 0 : 1, s_merge[threadIdx.x >> 6]);
         u += j1 - j0;
-    }
-}
-
-// ---------------------------------------------------------------- merge of split runs
-
-struct MergeArgs {
-    const int32_t* seq_prefix;
-    const float* part_lse;
-    const float* part_o;
-    uint8_t* out;
-    int32_t num_seqs;
-    int32_t num_q_heads;
-    int32_t num_kv_heads;
-    int32_t group;
-    int32_t num_workers;
-};
-
-__device__ inline int64_t run_start(int64_t w, int64_t U, int64_t W) { return w * U / W; }
-
-// The worker whose run holds unit u.
-__device__ inline int64_t owner_of(int64_t u, int64_t U, int64_t W) { return ((u + 1) * W + U - 1) / U - 1; }
-
-template <int DT, int D>
-__global__ __launch_bounds__(kGroupThreads) void merge_kernel(MergeArgs a) {
-    constexpr int E = DT == PA_F32 ? 4 : 2;
-    const int z = blockIdx.x;
-    const int Hkv = a.num_kv_heads, G = a.group, S = a.num_seqs;
-    const int s = z / Hkv, kvh = z % Hkv;
-    const int nb = a.seq_prefix[s + 1] - a.seq_prefix[s];
-    if (nb == 0) return;
-    const int64_t U = (int64_t)a.seq_prefix[S] * Hkv, W = a.num_workers;
-    const int64_t first = (int64_t)a.seq_prefix[s] * Hkv + (int64_t)kvh * nb;
-    const int64_t last = first + nb - 1;
-    const int64_t wa = owner_of(first, U, W), wb = owner_of(last, U, W);
-    if (wa == wb) return;  // one worker held the whole context and wrote out
-
-    // Each thread merges 4 consecutive dims of one head across the parts.
-    for (int i = threadIdx.x; i < G * D / 4; i += kGroupThreads) {
-        const int h = i / (D / 4), d4 = (i % (D / 4)) * 4;
-        float M = -INFINITY;
-        for (int64_t w = wa; w <= wb; ++w) {
-            if (run_start(w, U, W) == run_start(w + 1, U, W)) continue;
-            const int slot = (w == wa && run_start(w, U, W) != first) ? 1 : 0;
-            M = fmaxf(M, a.part_lse[((size_t)w * 2 + slot) * G + h]);
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        float den = 0.f;
-        for (int64_t w = wa; w <= wb; ++w) {
-            if (run_start(w, U, W) == run_start(w + 1, U, W)) continue;
-            const int slot = (w == wa && run_start(w, U, W) != first) ? 1 : 0;
-            const size_t part = ((size_t)w * 2 + slot) * G + h;
-            const float wt = __builtin_amdgcn_exp2f(a.part_lse[part] - M);
-            acc += wt * *reinterpret_cast<const f32x4*>(a.part_o + part * D + d4);
-            den += wt;
-        }
-        uint8_t* dst = a.out + (((size_t)s * a.num_q_heads + kvh * G + h) * D + d4) * E;
-        store4<DT>(dst, acc * (1.f / den));
     }
 }
 
@@ -506,9 +750,9 @@ struct WriteArgs {
 };
 
 // One workgroup per token.  K moves in 16-byte pieces (a piece of a row is
-// contiguous in the pool); V moves element by element into its transposed tile.
+// contiguous in the pool); V moves element by element into its transposed slab.
 template <int ELT>
-__global__ __launch_bounds__(kGroupThreads) void write_kernel(WriteArgs a) {
+__global__ __launch_bounds__(kWriteThreads) void write_kernel(WriteArgs a) {
     const int i = blockIdx.x;
     const int64_t slot = a.slots[i];
     if (slot < 0 || slot >= a.pool_slots) return;
@@ -516,16 +760,23 @@ __global__ __launch_bounds__(kGroupThreads) void write_kernel(WriteArgs a) {
     const int64_t p = slot / B;
     const int o = (int)(slot % B);
     const int pieces = D * ELT / 16;
-    for (int c = threadIdx.x; c < Hkv * pieces; c += kGroupThreads) {
+    const int slabs = B / 16, sl = o / 16, os = o % 16;
+    // K slab: the 16-byte piece dc of token t at (dc*16 + t)*16 bytes.
+    for (int c = threadIdx.x; c < Hkv * pieces; c += kWriteThreads) {
         const int g = c / pieces, dc = c % pieces;
         const uint4 v = *reinterpret_cast<const uint4*>(a.k_new + ((size_t)i * Hkv + g) * (size_t)(D * ELT) + dc * 16);
-        *reinterpret_cast<uint4*>(a.k_cache + (((size_t)p * Hkv + g) * pieces + dc) * (size_t)(B * 16) + o * 16) = v;
+        const size_t slab = ((size_t)p * Hkv + g) * slabs + sl;
+        *reinterpret_cast<uint4*>(a.k_cache + ((slab * pieces + dc) * 16 + os) * 16) = v;
     }
+    // V slab: element (t, d) at ((((d/16Y)*16 + d%16)*4 + t/4)*Y + (d/16)%Y)*4 + t%4, Y = 4/ELT.
     using U = typename std::conditional<ELT == 4, uint32_t, uint16_t>::type;
-    for (int e = threadIdx.x; e < Hkv * D; e += kGroupThreads) {
+    constexpr int Y = 4 / ELT;
+    for (int e = threadIdx.x; e < Hkv * D; e += kWriteThreads) {
         const int g = e / D, d = e % D;
         const U v = reinterpret_cast<const U*>(a.v_new)[((size_t)i * Hkv + g) * D + d];
-        reinterpret_cast<U*>(a.v_cache)[(((size_t)p * Hkv + g) * D + d) * B + o] = v;
+        const size_t slab = ((size_t)p * Hkv + g) * slabs + sl;
+        const int in_slab = ((((d / (16 * Y)) * 16 + d % 16) * 4 + os / 4) * Y + (d / 16) % Y) * 4 + os % 4;
+        reinterpret_cast<U*>(a.v_cache)[slab * 16 * D + in_slab] = v;
     }
 }
 
@@ -547,6 +798,27 @@ pa_status_t cu_count(int* out) {
     if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
         return PA_ERR_HIP;
     if (dev >= 0 && dev < 64) g_cu_count[dev].store(c, std::memory_order_relaxed);
+    *out = c;
+    return PA_OK;
+}
+
+std::atomic<int> g_lds_limit[64];
+
+// Largest LDS allocation (bytes) one workgroup may make on the current device.
+pa_status_t lds_limit(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    if (dev >= 0 && dev < 64) {
+        int c = g_lds_limit[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return PA_OK;
+        }
+    }
+    int c = 0;
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || c <= 0)
+        return PA_ERR_HIP;
+    if (dev >= 0 && dev < 64) g_lds_limit[dev].store(c, std::memory_order_relaxed);
     *out = c;
     return PA_OK;
 }
@@ -588,6 +860,7 @@ pa_status_t check_decode_shapes(int32_t num_seqs, int32_t num_q_heads, int32_t m
 }
 
 // Worker count and workspace layout; needs the device only for the automatic choice.
+// Workspace: arrival words [S * Hkv] (8 B each), then part_lse [W][2][G], then part_o [W][2][G][D].
 pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, const pa_cache_desc_t* cache,
                       int32_t num_workers, Plan* plan) {
     const int Hkv = cache->num_kv_heads, G = num_q_heads / Hkv, D = cache->head_dim;
@@ -609,13 +882,23 @@ pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
         W = (int)(want < 1 ? 1 : (want > cap ? cap : want));
     }
     plan->workers = W;
-    const size_t prefix = round_up(sizeof(int32_t) * ((size_t)num_seqs + 1), 256);
+    const size_t arrivals = round_up(sizeof(unsigned long long) * (size_t)num_seqs * Hkv, 256);
     const size_t lse = round_up(sizeof(float) * (size_t)W * 2 * G, 256);
     const size_t o = sizeof(float) * (size_t)W * 2 * G * D;
-    plan->off_lse = prefix;
-    plan->off_o = prefix + lse;
-    plan->bytes = prefix + lse + o;
+    plan->off_lse = arrivals;
+    plan->off_o = arrivals + lse;
+    plan->bytes = arrivals + lse + o;
     return PA_OK;
+}
+
+std::atomic<uint32_t> g_call_tag{0x2545f491u};
+
+uint32_t next_tag() {
+    uint32_t t;
+    do {
+        t = g_call_tag.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (t == 0);
+    return t;
 }
 
 template <int DT, int D, int B>
@@ -623,15 +906,9 @@ hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stre
     const int groups = (plan.workers + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups == 0) return hipSuccess;
     void* args[] = {const_cast<DecodeArgs*>(&a)};
-    const size_t lds = sizeof(int32_t) * ((size_t)a.num_seqs + 1);
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, B>), dim3(groups),
-                                   dim3(kGroupThreads), args, lds, stream);
-    if (e != hipSuccess || plan.per_segment) return e;
-    MergeArgs m{a.seq_prefix, a.part_lse, a.part_o, a.out, a.num_seqs, a.num_q_heads, a.num_kv_heads, a.group,
-                a.num_workers};
-    void* margs[] = {&m};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&merge_kernel<DT, D>), dim3(a.num_seqs * a.num_kv_heads),
-                           dim3(kGroupThreads), margs, 0, stream);
+    const size_t lds = sizeof(int32_t) * (2 * (size_t)a.num_seqs + 1);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, B>), dim3(groups),
+                           dim3(kGroupThreads), args, lds, stream);
 }
 
 template <int DT>
@@ -684,7 +961,7 @@ pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slo
     void* args[] = {&a};
     const void* fn = cache->dtype == PA_F32 ? reinterpret_cast<const void*>(&write_kernel<4>)
                                             : reinterpret_cast<const void*>(&write_kernel<2>);
-    hipError_t e = hipLaunchKernel(fn, dim3(num_tokens), dim3(kGroupThreads), args, 0,
+    hipError_t e = hipLaunchKernel(fn, dim3(num_tokens), dim3(kWriteThreads), args, 0,
                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
@@ -730,7 +1007,8 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.out = static_cast<uint8_t*>(out);
-    a.seq_prefix = plan.per_segment ? nullptr : reinterpret_cast<int32_t*>(ws);
+    a.arrivals = plan.per_segment ? nullptr : reinterpret_cast<unsigned long long*>(ws);
+    a.tag = next_tag();
     a.part_lse = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_lse);
     a.part_o = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_o);
     a.scale_log2 = scale * kLog2e;
@@ -742,6 +1020,12 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
     a.num_blocks = cache->num_blocks;
     a.num_workers = plan.workers;
     a.per_segment = plan.per_segment;
+
+    // LDS of one decode workgroup: lengths and prefix (dynamic) plus the merge areas (static).
+    int lds_max = 0;
+    st = lds_limit(&lds_max);
+    if (st != PA_OK) return st;
+    if (sizeof(int32_t) * (2 * (size_t)num_seqs + 1) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;

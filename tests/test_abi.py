@@ -108,18 +108,19 @@ def test_workspace_sizes():
     d = _desc(head_dim=128, num_kv_heads=8)
     # one wavefront per (sequence, kv-head): no workspace
     assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), -1) == 0
-    # stream split: prefix + 2 parts per worker of G lse values and G*D outputs
-    W, S, G, D = 100, 64, 4, 128
+    # stream split: an 8-byte arrival word per (sequence, kv-head), then
+    # 2 parts per worker of G lse values and G*D outputs
+    W, S, G, D, Hkv = 100, 64, 4, 128, 8
     got = L.pa_decode_workspace_bytes_ex(S, 32, 256, ctypes.byref(d), W)
     r = lambda x: (x + 255) // 256 * 256
-    assert got == r(4 * (S + 1)) + r(4 * W * 2 * G) + 4 * W * 2 * G * D
+    assert got == r(8 * S * Hkv) + r(4 * W * 2 * G) + 4 * W * 2 * G * D
     # rejected shapes report 0
     assert L.pa_decode_workspace_bytes_ex(64, 33, 256, ctypes.byref(d), W) == 0
 
 
 def test_binding_refuses_cpu_tensors():
     import torch
-    k, v = torch.zeros(2, 2, 8, 16, 8, dtype=torch.bfloat16), torch.zeros(2, 2, 64, 16, dtype=torch.bfloat16)
+    k, v = torch.zeros(2, 2, 1, 1024, dtype=torch.bfloat16), torch.zeros(2, 2, 1, 1024, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pa.write_kv(torch.zeros(1, 2, 64, dtype=torch.bfloat16), torch.zeros(1, 2, 64, dtype=torch.bfloat16),
                     torch.zeros(1, dtype=torch.int64), k, v)

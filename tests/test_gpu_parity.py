@@ -170,3 +170,61 @@ def test_zero_sequences_is_a_noop():
     import paged_kv_decode_slot_amd as pa
     out = pa.decode(g.q[:0], g.k_cache, g.v_cache, g.bt[:0], g.ctx[:0], case.scale)
     assert out.shape == (0, 4, 64)
+
+
+def _split_case():
+    return W.make_case(S=12, Hq=8, Hkv=2, D=128, B=16, dtype="bf16", ctx_range=(200, 1500), seed=61)
+
+
+def test_workspace_needs_no_initialisation():
+    """The merge bookkeeping tolerates any prior workspace contents."""
+    import paged_kv_decode_slot_amd as pa
+    case = _split_case()
+    g = GpuCase(case)
+    g.append()
+    ref = oracle.decode_case(case)
+    desc = pa.cache_desc(g.k_cache, g.v_cache)
+    for workers in (0, 37, 700):
+        need = pa.workspace_bytes(case.S, case.Hq, case.max_blocks_per_seq, desc, workers)
+        for fill in (0x00, 0xFF, 0x5A):
+            ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda:0")
+            out = pa.decode(g.q, g.k_cache, g.v_cache, g.bt, g.ctx, case.scale, num_workers=workers, workspace=ws)
+            torch.cuda.synchronize()
+            assert max_abs_err(out, ref) <= TOL["bf16"]
+        # random bytes, then the same workspace again and again
+        ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda:0")
+        first = None
+        for _ in range(4):
+            out = pa.decode(g.q, g.k_cache, g.v_cache, g.bt, g.ctx, case.scale, num_workers=workers, workspace=ws)
+            torch.cuda.synchronize()
+            assert max_abs_err(out, ref) <= TOL["bf16"]
+            if first is None:
+                first = out.clone()
+            assert torch.equal(dev_bits(out), dev_bits(first))
+
+
+def test_graph_replay_matches_eager():
+    """A captured decode replays correctly (same call tag on every replay)."""
+    import paged_kv_decode_slot_amd as pa
+    case = _split_case()
+    g = GpuCase(case)
+    g.append()
+    out = torch.empty_like(g.q)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        call = pa.prepare_decode(g.q, g.k_cache, g.v_cache, g.bt, g.ctx, case.scale, out, num_workers=300)
+        call()
+        stream.synchronize()
+        eager = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            call()
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dev_bits(out), dev_bits(eager)), f"replay {i}"
+        # eager work on the same workspace between replays
+        call()
+        torch.cuda.synchronize()

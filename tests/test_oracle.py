@@ -25,23 +25,37 @@ def _case(**kw):
 
 
 # --- P1: the write, against the documented pool shapes (torch views, not the oracle's index code) ---
+# Pools hold each block as 16-token slabs of 16*D elements.  Per slab, with
+# X = 16/elt and Y = 4/elt: K is [D/X][16][X]; V is [D/(16Y)][16][4][Y][4],
+# indexed by (d // 16Y, d % 16, t // 4, (d // 16) % Y, t % 4).
+
+def k_row(c, k_pool, p, o):
+    X = 16 // c.elt
+    kv = k_pool.view(c.num_blocks, c.Hkv, c.B // 16, c.D // X, 16, X)
+    return kv[p, :, o // 16, :, o % 16, :].reshape(c.Hkv, c.D)
+
+
+def v_row(c, v_pool, p, o):
+    Y = 4 // c.elt
+    vv = v_pool.view(c.num_blocks, c.Hkv, c.B // 16, c.D // (16 * Y), 16, 4, Y, 4)
+    d = torch.arange(c.D)
+    t = o % 16
+    return vv[p, :, o // 16][:, d // (16 * Y), d % 16, t // 4, (d // 16) % Y, t % 4]
+
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("B", [16, 32])
 def test_write_places_rows_at_documented_positions(dtype, B):
     c = _case(dtype=dtype, B=B, D=64, Hkv=2, Hq=4, S=5, ctx_range=(1, 3 * B + 5), seed=3)
     k_pool, v_pool = oracle.build_pools(c)
-    X = 16 // c.elt
-    kv = k_pool.view(c.num_blocks, c.Hkv, c.D // X, c.B, X)
-    vv = v_pool.view(c.num_blocks, c.Hkv, c.D, c.B)
     k_all, v_all, slots = c.all_tokens()
     written = 0
     for i, sl in enumerate(slots):
         if sl < 0:
             continue
         p, o = int(sl) // c.B, int(sl) % c.B
-        got_k = kv[p, :, :, o, :].reshape(c.Hkv, c.D)
-        got_v = vv[p, :, :, o]
+        got_k = k_row(c, k_pool, p, o)
+        got_v = v_row(c, v_pool, p, o)
         assert torch.equal(got_k.contiguous().view(torch.uint8), k_all[i].contiguous().view(torch.uint8))
         assert torch.equal(got_v.contiguous().view(torch.uint8), v_all[i].contiguous().view(torch.uint8))
         written += 1
@@ -61,8 +75,7 @@ def test_write_skips_negative_slots_and_is_last_writer_wins():
     v = torch.randn(3, c.Hkv, c.D)
     slots = np.array([-1, 7, 7], dtype=np.int64)
     oracle.write_kv(k, v, slots, k_pool, v_pool, num_blocks=c.num_blocks, B=c.B)
-    vv = v_pool.view(c.num_blocks, c.Hkv, c.D, c.B)
-    assert torch.equal(vv[0, :, :, 7], v[2])
+    assert torch.equal(v_row(c, v_pool, 0, 7), v[2])
     assert int(torch.isnan(k_pool).logical_not().sum()) == c.Hkv * c.D
 
 
@@ -166,9 +179,9 @@ def _brute(q, ks, vs, scale):
     return [float(sum(ei * Decimal(float(v[d])) for ei, v in zip(e, vs)) / den) for d in range(len(q))]
 
 
-@pytest.mark.parametrize("dtype,D", [("f32", 4), ("f16", 8), ("bf16", 8)])
+@pytest.mark.parametrize("dtype,D", [("f32", 16), ("f16", 32), ("bf16", 32)])
 def test_bruteforce_tiny(dtype, D):
-    c = _case(S=2, Hq=2, Hkv=1, D=D, B=2, dtype=dtype, ctx=[5, 3], ctx_range=None, seed=21)
+    c = _case(S=2, Hq=2, Hkv=1, D=D, B=16, dtype=dtype, ctx=[5, 3], ctx_range=None, seed=21)
     got = oracle.decode_case(c)
     for s in range(c.S):
         k, v = c.logical_kv(s)
