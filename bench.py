@@ -127,6 +127,30 @@ def measure(n, args, device):
     return res
 
 
+# Measured HBM traffic of the decode kernel (two rocprofv3 counter passes, scaled by a
+# plain copy of known size), kept with the hash of the source it was measured on.
+TRAFFIC_FILES = {3: "profiles/decode_kernel_C3_llama3-8b_bf16_counters.txt"}
+KERNEL_SOURCE = "paged_kv_decode_slot_amd/csrc/pagedattn.hip"
+
+
+def measured_traffic(config: int):
+    """Bytes per decode launch from the counter summary, or None if there is none or the kernel changed since."""
+    import hashlib
+
+    path = TRAFFIC_FILES.get(config)
+    if path is None or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    fields = {}
+    for line in open(os.path.join(ROOT, path)):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = hashlib.sha256(open(os.path.join(ROOT, KERNEL_SOURCE), "rb").read()).hexdigest()
+    if fields.get("source_sha256") != src or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(case, min_seconds):
     import oracle
     from paged_kv_decode_slot_amd import workloads as W
@@ -238,7 +262,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(main_res["decode_gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.config),
+            "traffic_unit": "bytes per launch",
             "bytes_per_launch": main_res["decode_bytes"],
             "launch_us_mean": round(dec_us, 2),
         },
