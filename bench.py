@@ -38,6 +38,7 @@ def log(msg):
 
 
 def setup_layers(case, layers, device, num_workers):
+    """Per layer: (append call, decode call, fused step call) on that layer's own pools."""
     import torch
 
     import paged_kv_decode_slot_amd as pa
@@ -61,34 +62,59 @@ def setup_layers(case, layers, device, num_workers):
         kc, vc = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
         out = torch.empty_like(q)
         steps.append((pa.prepare_write_kv(k_new, v_new, slot_new, kc, vc),
-                      pa.prepare_decode(q, kc, vc, bt, ctx, case.scale, out, num_workers=num_workers)))
+                      pa.prepare_decode(q, kc, vc, bt, ctx, case.scale, out, num_workers=num_workers),
+                      pa.prepare_decode_append(q, k_new, v_new, kc, vc, bt, ctx, case.scale, out,
+                                               num_workers=num_workers)))
     torch.cuda.synchronize()
     return steps
 
 
-def time_steps(steps, n_steps, warmup):
+def _events(n):
+    import torch
+
+    return [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+
+
+def time_two_calls(steps, n_steps, warmup):
+    """pa_write_kv then pa_decode per step; per-step events around each call."""
     import torch
 
     for i in range(warmup):
-        w, d = steps[i % len(steps)]
+        w, d, _ = steps[i % len(steps)]
         w()
         d()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
-    t0 = time.perf_counter()
+    ev = _events(n_steps)
     for i in range(n_steps):
-        w, d = steps[i % len(steps)]
+        w, d, _ = steps[i % len(steps)]
         ev[i][0].record()
         w()
         ev[i][1].record()
         d()
         ev[i][2].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     t_write = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_steps)]  # us
     t_decode = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(n_steps)]
     total_ms = ev[0][0].elapsed_time(ev[-1][2])
-    return t_write, t_decode, total_ms, wall
+    return t_write, t_decode, total_ms
+
+
+def time_fused(steps, n_steps, warmup):
+    """pa_decode_append per step (the whole step in one launch); per-step events."""
+    import torch
+
+    for i in range(warmup):
+        steps[i % len(steps)][2]()
+    torch.cuda.synchronize()
+    ev = _events(n_steps)
+    for i in range(n_steps):
+        ev[i][0].record()
+        steps[i % len(steps)][2]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t_step = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_steps)]
+    total_ms = ev[0][0].elapsed_time(ev[-1][1])
+    return t_step, total_ms
 
 
 def pct(xs, p):
@@ -106,38 +132,42 @@ def measure(n, args, device):
     layers = args.layers or max(2, math.ceil(2 * 2**30 / layer_bytes))
     steps = setup_layers(case, layers, device, args.workers)
     log(f"[bench] workload {n}: {layers} layers of {layer_bytes / 1e9:.2f} GB; timing {args.steps} steps")
-    t_write, t_decode, total_ms, wall = time_steps(steps, args.steps, args.warmup)
+    t_step, fused_ms = time_fused(steps, args.steps, args.warmup)
+    t_write, t_decode, split_ms = time_two_calls(steps, args.steps, args.warmup)
     dec_b, wr_b = W.decode_bytes(case), W.write_bytes(case)
-    ms_per_step = total_ms / args.steps
+    step_mean = statistics.fmean(t_step)
     dec_mean = statistics.fmean(t_decode)
-    res = dict(
+    return dict(
         case=case,
-        ms_per_step=ms_per_step,
-        step_gbs=(dec_b + wr_b) / (ms_per_step * 1e-3) / 1e9,
+        layers=layers,
         decode_bytes=dec_b,
         write_bytes=wr_b,
+        # the fused step: pa_decode_append
+        ms_per_step=fused_ms / args.steps,
+        step_us=dict(mean=step_mean, p10=pct(t_step, 10), p50=pct(t_step, 50), p90=pct(t_step, 90)),
+        step_gbs=(dec_b + wr_b) / (step_mean * 1e-6) / 1e9,
+        seq_heads_per_s=case.S * case.Hq / (step_mean * 1e-6),
+        # the same step as two calls: pa_write_kv, then pa_decode
+        two_call_ms_per_step=split_ms / args.steps,
         t_decode_us=dict(mean=dec_mean, p10=pct(t_decode, 10), p50=pct(t_decode, 50), p90=pct(t_decode, 90)),
         t_write_us=dict(mean=statistics.fmean(t_write), p50=pct(t_write, 50)),
         t_layer_us_p50=pct([a + b for a, b in zip(t_write, t_decode)], 50),
         decode_gbs=dec_b / (dec_mean * 1e-6) / 1e9,
-        seq_heads_per_s=case.S * case.Hq / (dec_mean * 1e-6),
-        layers=layers,
-        wall_s=wall,
     )
-    return res
 
 
 # Measured HBM traffic of the decode kernel (two rocprofv3 counter passes, scaled by a
 # plain copy of known size), kept with the hash of the source it was measured on.
-TRAFFIC_FILES = {3: "profiles/decode_kernel_C3_llama3-8b_bf16_counters.txt"}
+TRAFFIC_FILES = {(3, "fused"): "profiles/decode_append_kernel_C3_llama3-8b_bf16_counters.txt",
+                 (3, "decode"): "profiles/decode_kernel_C3_llama3-8b_bf16_counters.txt"}
 KERNEL_SOURCE = "paged_kv_decode_slot_amd/csrc/pagedattn.hip"
 
 
-def measured_traffic(config: int):
-    """Bytes per decode launch from the counter summary, or None if there is none or the kernel changed since."""
+def measured_traffic(config: int, kind: str):
+    """Bytes per launch from a counter summary, or None if there is none or the kernel changed since."""
     import hashlib
 
-    path = TRAFFIC_FILES.get(config)
+    path = TRAFFIC_FILES.get((config, kind))
     if path is None or not os.path.exists(os.path.join(ROOT, path)):
         return None
     fields = {}
@@ -219,13 +249,15 @@ def main():
             continue
         r = measure(n, args, device)
         c = r.pop("case")
-        other[f"C{n}"] = dict(workload=W.CONFIGS[n]["name"], t_decode_us_mean=round(r["t_decode_us"]["mean"], 2),
-                              t_decode_us_p50=round(r["t_decode_us"]["p50"], 2),
-                              t_layer_us_p50=round(r["t_layer_us_p50"], 2),
-                              decode_gbs=round(r["decode_gbs"], 1),
-                              decode_frac_of_peak=round(r["decode_gbs"] / PEAK_HBM_GBS, 4),
-                              seq_heads_per_s=round(r["seq_heads_per_s"]), layers=r["layers"],
-                              decode_bytes=r["decode_bytes"], context_tokens=int(c.context_lens.sum()))
+        other[f"C{n}"] = dict(
+            workload=W.CONFIGS[n]["name"],
+            step_us_mean=round(r["step_us"]["mean"], 2), step_us_p50=round(r["step_us"]["p50"], 2),
+            step_gbs=round(r["step_gbs"], 1), step_frac_of_peak=round(r["step_gbs"] / PEAK_HBM_GBS, 4),
+            two_call_t_decode_us_mean=round(r["t_decode_us"]["mean"], 2),
+            two_call_t_layer_us_p50=round(r["t_layer_us_p50"], 2),
+            decode_gbs=round(r["decode_gbs"], 1), decode_frac_of_peak=round(r["decode_gbs"] / PEAK_HBM_GBS, 4),
+            seq_heads_per_s=round(r["seq_heads_per_s"]), layers=r["layers"],
+            step_bytes=r["decode_bytes"] + r["write_bytes"], context_tokens=int(c.context_lens.sum()))
         del c, r
         torch.cuda.empty_cache()
 
@@ -234,7 +266,7 @@ def main():
         log("[bench] timing the CPU oracle on the host")
         cpu = cpu_baseline(case, args.cpu_seconds)
 
-    dec_us = main_res["t_decode_us"]["mean"]
+    step_bytes = main_res["decode_bytes"] + main_res["write_bytes"]
     line = {
         "metric": METRIC,
         "value": round(main_res["step_gbs"], 2),
@@ -252,29 +284,35 @@ def main():
             "workload": W.CONFIGS[args.config]["name"],
             "seqs": case.S, "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,
             "block_size": case.B, "context_tokens": int(case.context_lens.sum()),
-            "step": "pa_write_kv of one token per sequence, then pa_decode",
+            "step": "pa_decode_append: KV append of one token per sequence + decode attention, one launch",
             "layers_rotated": main_res["layers"], "workers": args.workers,
         },
         "roofline": {
-            "kernel": "decode_kernel (the single launch of pa_decode)",
+            "kernel": "decode_kernel with append (the single launch of pa_decode_append)",
             "bound": "hbm",
-            "achieved": round(main_res["decode_gbs"], 1),
+            "achieved": round(main_res["step_gbs"], 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(main_res["decode_gbs"] / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(args.config),
+            "frac": round(main_res["step_gbs"] / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(args.config, "fused"),
             "traffic_unit": "bytes per launch",
-            "bytes_per_launch": main_res["decode_bytes"],
-            "launch_us_mean": round(dec_us, 2),
+            "bytes_per_launch": step_bytes,
+            "launch_us_mean": round(main_res["step_us"]["mean"], 2),
         },
         "cpu_baseline": cpu,
         "detail": {
-            "t_decode_us": {k: round(v, 2) for k, v in main_res["t_decode_us"].items()},
-            "t_write_us": {k: round(v, 2) for k, v in main_res["t_write_us"].items()},
-            "t_layer_us_p50": round(main_res["t_layer_us_p50"], 2),
-            "decode_gbs": round(main_res["decode_gbs"], 1),
+            "step_us": {k: round(v, 2) for k, v in main_res["step_us"].items()},
             "seq_heads_per_s": round(main_res["seq_heads_per_s"]),
-            "step_bytes": main_res["decode_bytes"] + main_res["write_bytes"],
+            "step_bytes": step_bytes,
+            "two_calls": {
+                "ms_per_step": round(main_res["two_call_ms_per_step"], 5),
+                "t_write_us": {k: round(v, 2) for k, v in main_res["t_write_us"].items()},
+                "t_decode_us": {k: round(v, 2) for k, v in main_res["t_decode_us"].items()},
+                "t_layer_us_p50": round(main_res["t_layer_us_p50"], 2),
+                "decode_gbs": round(main_res["decode_gbs"], 1),
+                "decode_frac_of_peak": round(main_res["decode_gbs"] / PEAK_HBM_GBS, 4),
+                "decode_traffic": measured_traffic(args.config, "decode"),
+            },
             "other": other,
         },
     }

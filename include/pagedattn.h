@@ -38,10 +38,11 @@
  * Inside a slab, with t = o % 16, X = 16 / element bytes (4 for f32, 8 for
  * f16/bf16) and Y = 4 / element bytes (1 for f32, 2 for f16/bf16), dim `d` is
  *    K: (d / X) * 16 * X + t * X + d % X
- *    V: ((((d / (16*Y)) * 16 + d % 16) * 4 + t / 4) * Y + (d / 16) % Y) * 4 + t % 4
- * (for f32 the V slab is simply the transpose, d * 16 + t).  This places each
- * 16-byte piece that a matrix-core operand needs in one load, with
- * consecutive lanes reading consecutive bytes.  A slot is p * block_size + o.
+ *    V: ((((t / 4) * (D / (16*Y)) + d / (16*Y)) * 16 + d % 16) * Y + (d / 16) % Y) * 4 + t % 4
+ * (for f32: ((t / 4) * D + d) * 4 + t % 4).  This places each 16-byte piece
+ * that a matrix-core operand needs in one load, with consecutive lanes
+ * reading consecutive bytes, and keeps a token's V row inside one quarter of
+ * its slab.  A slot is p * block_size + o.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -145,7 +146,28 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
                          size_t workspace_bytes, int32_t num_workers, pa_stream_t stream);
 
-/* Workspace bytes pa_decode_ex needs for that num_workers. */
+/*
+ * One decode step in one launch: the KV append of each sequence's new token
+ * followed by decode attention, with the same results as
+ *    pa_write_kv(k_new, v_new, slots, k_cache, v_cache, num_seqs, ...)
+ *    pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, ...)
+ * where the new token of sequence s is its last position, L - 1 with
+ * L = context_lens[s], so slots[s] = block_tables[s][(L-1)/block_size] *
+ * block_size + (L-1) % block_size (no slot when L == 0).  The decode output
+ * is bitwise the same as that pair of calls with the same num_workers, and
+ * so are the caches afterwards.
+ *   k_new, v_new : [num_seqs][num_kv_heads][head_dim], 16-byte aligned
+ *   other arguments as in pa_decode_ex; the caches are written.
+ * Precondition (unchecked): no sequence's new-token slot lies in a block
+ * another sequence of the call reads (distinct last blocks).
+ */
+pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                             const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
+                             int32_t num_workers, pa_stream_t stream);
+
+/* Workspace bytes pa_decode_ex and pa_decode_append need for that num_workers. */
 size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                     const pa_cache_desc_t* cache, int32_t num_workers);
 

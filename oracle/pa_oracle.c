@@ -33,8 +33,8 @@
  * contiguous elements.  With X = 16 / element_bytes and Y = 4 / element_bytes,
  * token t (0..15) and dim d of a slab sit at
  *    K: (d / X) * 16 * X + t * X + d % X
- *    V: ((((d / (16*Y)) * 16 + d % 16) * 4 + t / 4) * Y + (d / 16) % Y) * 4 + t % 4
- * (for f32, Y = 1 and V is simply d * 16 + t: the slab transposed), and slab
+ *    V: ((((t / 4) * (D / (16*Y)) + d / (16*Y)) * 16 + d % 16) * Y + (d / 16) % Y) * 4 + t % 4
+ * (for f32, Y = 1 and V is ((t / 4) * D + d) * 4 + t % 4), and slab
  * (p, g, o / 16) starts at element ((p * Hkv + g) * (B / 16) + o / 16) * 16 * D.
  */
 #include <math.h>
@@ -87,8 +87,8 @@ static size_t k_index(int64_t p, int g, int o, int d, int Hkv, int B, int D, int
 
 static size_t v_index(int64_t p, int g, int o, int d, int Hkv, int B, int D, int Y) {
     int t = o % 16;
-    size_t in_slab = ((((size_t)(d / (16 * Y)) * 16 + (size_t)(d % 16)) * 4 + (size_t)(t / 4)) * Y +
-                      (size_t)((d / 16) % Y)) * 4 + (size_t)(t % 4);
+    size_t q = (size_t)(t / 4) * (size_t)(D / (16 * Y)) + (size_t)(d / (16 * Y)); /* (token quad, 16Y-dim group) */
+    size_t in_slab = ((q * 16 + (size_t)(d % 16)) * Y + (size_t)((d / 16) % Y)) * 4 + (size_t)(t % 4);
     return slab_base(p, g, o, Hkv, B, D) + in_slab;
 }
 

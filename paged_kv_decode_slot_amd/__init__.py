@@ -10,10 +10,12 @@ from .binding import (  # noqa: F401
     cache_desc,
     cache_shapes,
     decode,
+    decode_append,
     lib,
     library_path,
     new_cache,
     prepare_decode,
+    prepare_decode_append,
     prepare_write_kv,
     workspace_bytes,
     write_kv,

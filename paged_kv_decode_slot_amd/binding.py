@@ -24,6 +24,7 @@ EXPORTS = (
     "pa_write_kv",
     "pa_decode",
     "pa_decode_ex",
+    "pa_decode_append",
     "pa_decode_workspace_bytes",
     "pa_decode_workspace_bytes_ex",
     "pa_status_string",
@@ -65,6 +66,8 @@ def lib() -> ctypes.CDLL:
         L.pa_decode.restype = ctypes.c_int
         L.pa_decode_ex.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, I32, P]
         L.pa_decode_ex.restype = ctypes.c_int
+        L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, I32, P]
+        L.pa_decode_append.restype = ctypes.c_int
         L.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, DP]
         L.pa_decode_workspace_bytes.restype = SZ
         L.pa_decode_workspace_bytes_ex.argtypes = [I32, I32, I32, DP, I32]
@@ -234,6 +237,50 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=N
 
     def call():
         _check("pa_decode", fn(*args))
+        return keep[5]
+
+    return call
+
+
+def _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_workers, workspace):
+    dev, out, dargs, keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                                         num_workers, workspace)
+    desc = keep[7]
+    S = q.shape[0]
+    for t in (k_new, v_new):
+        if t.device != dev or t.dtype != q.dtype or not t.is_contiguous() \
+                or tuple(t.shape) != (S, desc.num_kv_heads, desc.head_dim):
+            raise ValueError("k_new/v_new must be contiguous [S, Hkv, D] in the cache dtype on the same device")
+    # pa_decode_ex arguments are (q, k, v, bt, ctx, scale, out, S, Hq, maxblk, desc, ws, ws_bytes, workers, stream)
+    q_p, k_p, v_p, bt_p, ctx_p, sc, out_p, S_, Hq, maxblk, descp, ws_p, ws_n, wk, st = dargs
+    args = (q_p, k_new.data_ptr(), v_new.data_ptr(), k_p, v_p, bt_p, ctx_p, sc, out_p, S_, Hq, maxblk, descp,
+            ws_p, ws_n, wk, st)
+    return dev, out, args, keep + (k_new, v_new)
+
+
+def decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                  v_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                  out: torch.Tensor | None = None, *, num_workers: int = 0,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one launch: append each sequence's new token (position ctx-1, its
+    block-table slot) and attend; same results as write_kv then decode."""
+    dev, out, args, _keep = _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                                         out, num_workers, workspace)
+    with torch.cuda.device(dev):
+        st = lib().pa_decode_append(*args)
+    _check("pa_decode_append", st)
+    return out
+
+
+def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out=None, *,
+                          num_workers=0, workspace=None):
+    """Validate once; return a no-argument callable issuing the same pa_decode_append."""
+    _dev_, out, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                                          out, num_workers, workspace)
+    fn = lib().pa_decode_append
+
+    def call():
+        _check("pa_decode_append", fn(*args))
         return keep[5]
 
     return call

@@ -209,6 +209,10 @@ struct DecodeArgs {
     unsigned long long* arrivals;  // [num_seqs * Hkv]: (call tag << 32) | parts stored so far
     float* part_lse;               // [workers][2][G]
     float* part_o;                 // [workers][2][G][D]
+    const uint8_t* k_new;          // append: [num_seqs][Hkv][D], the token at position ctx-1
+    const uint8_t* v_new;
+    uint8_t* k_cache_w;            // append: the same pools, written
+    uint8_t* v_cache_w;
     float scale_log2;
     uint32_t tag;  // nonzero; differs between consecutive calls
     int32_t num_seqs;
@@ -219,6 +223,7 @@ struct DecodeArgs {
     int32_t num_blocks;
     int32_t num_workers;
     int32_t per_segment;  // 1: worker w owns (sequence, kv-head) w entirely
+    int32_t attn_groups;  // append: workgroups [attn_groups, grid) store the new rows
 };
 
 __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
@@ -332,6 +337,11 @@ typedef const int32_t __attribute__((address_space(4)))* ScalarPtr;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// A 16-byte store with the non-temporal hint.
+__device__ inline void store_nt(uint8_t* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
 template <typename T>
 __device__ inline T load_kv(const uint8_t* p) {
 #if PA_KV_NONTEMPORAL
@@ -339,6 +349,28 @@ __device__ inline T load_kv(const uint8_t* p) {
 #else
     return *reinterpret_cast<const T*>(p);
 #endif
+}
+
+// Put one token's entries (token e of the piece's 4-token groups) into a V piece:
+// 16-bit types hold two dims per piece (halves .xy and .zw), f32 one.
+template <int ELT>
+__device__ inline void put_v_row(uint4& v, int e, const uint32_t* vals) {
+    if constexpr (ELT == 2) {
+        const int sh = (e & 1) * 16;
+        const uint32_t keep = ~(0xffffu << sh);
+        if (e < 2) {
+            v.x = (v.x & keep) | (vals[0] << sh);
+            v.z = (v.z & keep) | (vals[1] << sh);
+        } else {
+            v.y = (v.y & keep) | (vals[0] << sh);
+            v.w = (v.w & keep) | (vals[1] << sh);
+        }
+    } else {
+        if (e == 0) v.x = vals[0];
+        if (e == 1) v.y = vals[0];
+        if (e == 2) v.z = vals[0];
+        if (e == 3) v.w = vals[0];
+    }
 }
 
 template <int DT, int D, int B>
@@ -507,7 +539,7 @@ __device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int64_t F, int 
 // pair (s, kvh) occupies units [F, F + nb).  A run over the whole context
 // writes out; otherwise the run stores a partial in slot `slot` of worker w,
 // and the wave that stores the pair's last partial merges them.
-template <int DT, int D, int B>
+template <int DT, int D, int B, bool APPEND>
 __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0, int j1, int nb, int64_t F,
                            int64_t U, int64_t W, int w, int slot, MergeLds& mlds) {
     using C = Cfg<DT, D, B>;
@@ -524,16 +556,16 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     const ScalarPtr bt = (ScalarPtr)(a.block_tables + (size_t)s * a.max_blocks);
     int next_id = bt[j0];
 
-    // Q of the lane's head, in the B-operand form of the QK product.
+    // Q of the lane's head, in the B-operand form of the QK product.  Columns
+    // n >= G are padding: they take head 0's row, so they only repeat that
+    // head's scores (and its rescale decisions) and are never stored.  Every
+    // lane loads, so the load is not under a lane mask.
     uint4 qf[C::kKFrag];
     {
         const int hq = kvh * G + (n < G ? n : 0);
         const uint8_t* qrow = a.q + ((size_t)s * a.num_q_heads + hq) * (size_t)(D * E);
 #pragma unroll
-        for (int f = 0; f < C::kKFrag; ++f) {
-            uint4 v = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * r);
-            qf[f] = n < G ? v : make_uint4(0, 0, 0, 0);
-        }
+        for (int f = 0; f < C::kKFrag; ++f) qf[f] = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * r);
     }
 
     f32x4 O[C::kVChunk];
@@ -545,6 +577,38 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     const size_t blk_stride = (size_t)a.num_kv_heads * C::kTileBytes;
     const size_t head_off = (size_t)kvh * C::kTileBytes;
     const int ntiles = (j1 - j0) * C::kSub;
+
+    // Fused append: the run that holds the sequence's last block owns the new
+    // token (position ctx - 1).  It loads the token's K/V rows for this kv-head
+    // into the registers where its tile holds them and attends to them from
+    // there, so it never depends on the cache store of those rows, which
+    // other waves of the launch make (its tile load may see the slot before
+    // or after that store).  No other run reads that slot.
+    const bool owns_new = APPEND && j1 == nb && ctx > 0;
+    const int tl = ctx - 1;                        // position of the new token
+    const int tl_tile = (tl / B - j0) * C::kSub + (tl % B) / 16;  // its tile in this run
+    const int tt = tl % 16;                        // its row within that tile
+    uint4 k_sub[C::kKFrag];                        // lanes n == tt: the K pieces of the new row
+    uint32_t v_sub[C::kVPiece][4 / E];             // lanes r == tt/4: its V entries for this lane's dims
+    if constexpr (APPEND) {
+        if (owns_new) {
+            const size_t row = ((size_t)s * a.num_kv_heads + kvh) * (size_t)(D * E);
+            const uint8_t* kn = a.k_new + row;
+            const uint8_t* vn = a.v_new + row;
+#pragma unroll
+            for (int f = 0; f < C::kKFrag; ++f)
+                k_sub[f] = n == tt ? *reinterpret_cast<const uint4*>(kn + (4 * f + r) * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int c = 0; c < C::kVPiece; ++c)
+#pragma unroll
+                for (int h = 0; h < 4 / E; ++h) {
+                    const int d = c * (64 / E) + 16 * h + n;  // dim of this lane's row in half h of piece c
+                    v_sub[c][h] = r == tt / 4 ? (E == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(vn)[d]
+                                                        : reinterpret_cast<const uint32_t*>(vn)[d])
+                                              : 0u;
+                }
+        }
+    }
 
     int phys = 0;
     auto issue = [&](int tau, Tile<DT, D, B>& t) {
@@ -562,7 +626,7 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
             t.k[f] = __builtin_bit_cast(uint4, load_kv<u32x4>(kt + ((4 * f + r) * 16 + n) * 16));
 #pragma unroll
         for (int c = 0; c < C::kVPiece; ++c)
-            t.v[c] = __builtin_bit_cast(uint4, load_kv<u32x4>(vt + ((c * 16 + n) * 4 + r) * 16));
+            t.v[c] = __builtin_bit_cast(uint4, load_kv<u32x4>(vt + ((r * C::kVPiece + c) * 16 + n) * 16));
     };
 
     // m is a reference maximum, not necessarily the running one: weights are
@@ -575,6 +639,18 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
         const int j = j0 + tau / C::kSub, u = tau % C::kSub;
         const int tok0 = j * B + 16 * u + 4 * r;  // position of this lane's first row
         const bool partial = may_be_partial && j * B + 16 * u + 16 > ctx;
+        if constexpr (APPEND) {
+            if (may_be_partial && owns_new && tau == tl_tile) {  // the tile holding the new token
+                if (n == tt) {
+#pragma unroll
+                    for (int f = 0; f < C::kKFrag; ++f) t.k[f] = k_sub[f];
+                }
+                if (r == tt / 4) {
+#pragma unroll
+                    for (int c = 0; c < C::kVPiece; ++c) put_v_row<E>(t.v[c], tt % 4, v_sub[c]);
+                }
+            }
+        }
 
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -676,18 +752,100 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     if (__shfl(last, 0)) merge_parts<DT, D>(a, s, kvh, F, nb, U, W, mlds);
 }
 
+// Fused append, the store side: wave `wi` of the writer workgroups copies the
+// new K/V rows of RPW consecutive (sequence, kv-head) rows into their slots,
+// the same bytes pa_write_kv stores.  It runs beside the attention waves, so
+// their loads never wait behind these stores (a wave's loads and stores share
+// one counter).  The stores carry the non-temporal hint: each row touches one
+// line per 16-byte K piece and one per V line of its slab, and letting those
+// partial lines stream out instead of sitting dirty in L2 costs the reads
+// around them less.  A row with no context, or whose block id or length lies
+// outside the table or pool, is skipped.
+template <int DT, int D, int B>
+__device__ void store_new_rows(const DecodeArgs& a, int wi) {
+    using C = Cfg<DT, D, B>;
+    constexpr int E = C::kElt;
+    constexpr int KP = D * E / 16;  // 16-byte pieces per row
+    constexpr int RPW = 64 / KP;    // rows per wave: one piece per lane
+    constexpr int NV = RPW * D / 64;  // V elements per lane; element k of a lane is in row 64k / D
+    const int lane = threadIdx.x & 63;
+    const int Hkv = a.num_kv_heads;
+    const int rows = a.num_seqs * Hkv;
+    const int r0 = wi * RPW;
+    if (r0 >= rows) return;
+
+    // Byte offset of row `row`'s slab in either pool and the token's place in
+    // it, or -1 when the row has nothing to store.
+    auto locate = [&](int row, int& tt) -> int64_t {
+        if (row >= rows) return -1;
+        const int sq = row / Hkv, g = row % Hkv;
+        const int L = clamp_ctx(a.context_lens[sq], B, a.max_blocks);
+        if (L == 0) return -1;
+        const int pos = L - 1;
+        const int pl = a.block_tables[(size_t)sq * a.max_blocks + pos / B];
+        if ((unsigned)pl >= (unsigned)a.num_blocks) return -1;
+        tt = pos % 16;
+        return ((int64_t)pl * Hkv + g) * C::kTileBytes + (int64_t)((pos % B) / 16) * C::kSlabBytes;
+    };
+
+    // Loads first, so they are all in flight together.
+    const uint8_t* kn = a.k_new + (size_t)r0 * (D * E);
+    const uint8_t* vn = a.v_new + (size_t)r0 * (D * E);
+    const int kq = lane / KP, ki = lane % KP;
+    uint4 kv = make_uint4(0, 0, 0, 0);
+    if (r0 + kq < rows) kv = *reinterpret_cast<const uint4*>(kn + (size_t)lane * 16);
+    uint32_t vv[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        vv[k] = 0;
+        if (r0 + 64 * k / D < rows)
+            vv[k] = E == 2 ? (uint32_t)reinterpret_cast<const uint16_t*>(vn)[64 * k + lane]
+                           : reinterpret_cast<const uint32_t*>(vn)[64 * k + lane];
+    }
+
+    // K: lane (kq, ki) holds piece ki of row r0 + kq.
+    {
+        int tt = 0;
+        const int64_t slab = locate(r0 + kq, tt);
+        if (slab >= 0) store_nt(a.k_cache_w + slab + (ki * 16 + tt) * 16, kv);
+    }
+    // V: element k of the lane is dim (64k) % D + lane of row r0 + 64k / D.
+    constexpr int Y = 4 / E;
+#pragma unroll
+    for (int q = 0; q < RPW; ++q) {
+        int tt = 0;
+        const int64_t slab = locate(r0 + q, tt);
+        if (slab < 0) continue;
+#pragma unroll
+        for (int k = q * D / 64; k < (q + 1) * D / 64; ++k) {
+            const int d = (64 * k) % D + lane;
+            const int e = ((((tt / 4) * (D / (16 * Y)) + d / (16 * Y)) * 16 + d % 16) * Y + (d / 16) % Y) * 4 + tt % 4;
+            if constexpr (E == 2)
+                __builtin_nontemporal_store((uint16_t)vv[k], reinterpret_cast<uint16_t*>(a.v_cache_w + slab) + e);
+            else
+                __builtin_nontemporal_store(vv[k], reinterpret_cast<uint32_t*>(a.v_cache_w + slab) + e);
+        }
+    }
+}
+
 constexpr size_t kDecodeStaticLds = sizeof(MergeLds) * kWavesPerGroup + sizeof(int32_t) * kWavesPerGroup;
 
 #ifndef PA_MIN_WAVES_PER_SIMD
 #define PA_MIN_WAVES_PER_SIMD 1
 #endif
 
-template <int DT, int D, int B>
+template <int DT, int D, int B, bool APPEND>
 __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
     using C = Cfg<DT, D, B>;
     extern __shared__ int32_t s_lds[];  // ctx[num_seqs], pre[num_seqs + 1]
     __shared__ int32_t s_wave_tot[kWavesPerGroup];
     __shared__ MergeLds s_merge[kWavesPerGroup];
+    if constexpr (APPEND) {
+        if ((int)blockIdx.x >= a.attn_groups) {
+            store_new_rows<DT, D, B>(a, (blockIdx.x - a.attn_groups) * kWavesPerGroup + (threadIdx.x >> 6));
+            return;
+        }
+    }
     int32_t* s_ctx = s_lds;
     int32_t* s_pre = s_lds + a.num_seqs;
     load_lengths<B>(a, s_ctx, s_pre, s_wave_tot);
@@ -730,7 +888,8 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         const int64_t left = end - u;
         const int j1 = left < (int64_t)(nb - j0) ? j0 + (int)left : nb;
         const int64_t F = (int64_t)base * Hkv + (int64_t)kvh * nb;
-        attend_run<DT, D, B>(a, s, kvh, ctx, j0, j1, nb, F, U, W, w, u == start ? 0 : 1, s_merge[threadIdx.x >> 6]);
+        attend_run<DT, D, B, APPEND>(a, s, kvh, ctx, j0, j1, nb, F, U, W, w, u == start ? 0 : 1,
+                                     s_merge[threadIdx.x >> 6]);
         u += j1 - j0;
     }
 }
@@ -750,7 +909,7 @@ struct WriteArgs {
 };
 
 // One workgroup per token.  K moves in 16-byte pieces (a piece of a row is
-// contiguous in the pool); V moves element by element into its transposed slab.
+// contiguous in the pool); V moves element by element into its slab.
 template <int ELT>
 __global__ __launch_bounds__(kWriteThreads) void write_kernel(WriteArgs a) {
     const int i = blockIdx.x;
@@ -768,14 +927,14 @@ __global__ __launch_bounds__(kWriteThreads) void write_kernel(WriteArgs a) {
         const size_t slab = ((size_t)p * Hkv + g) * slabs + sl;
         *reinterpret_cast<uint4*>(a.k_cache + ((slab * pieces + dc) * 16 + os) * 16) = v;
     }
-    // V slab: element (t, d) at ((((d/16Y)*16 + d%16)*4 + t/4)*Y + (d/16)%Y)*4 + t%4, Y = 4/ELT.
+    // V slab: element (t, d) at ((((t/4)*(D/16Y) + d/16Y)*16 + d%16)*Y + (d/16)%Y)*4 + t%4, Y = 4/ELT.
     using U = typename std::conditional<ELT == 4, uint32_t, uint16_t>::type;
     constexpr int Y = 4 / ELT;
     for (int e = threadIdx.x; e < Hkv * D; e += kWriteThreads) {
         const int g = e / D, d = e % D;
         const U v = reinterpret_cast<const U*>(a.v_new)[((size_t)i * Hkv + g) * D + d];
         const size_t slab = ((size_t)p * Hkv + g) * slabs + sl;
-        const int in_slab = ((((d / (16 * Y)) * 16 + d % 16) * 4 + os / 4) * Y + (d / 16) % Y) * 4 + os % 4;
+        const int in_slab = ((((os / 4) * (D / (16 * Y)) + d / (16 * Y)) * 16 + d % 16) * Y + (d / 16) % Y) * 4 + os % 4;
         reinterpret_cast<U*>(a.v_cache)[slab * 16 * D + in_slab] = v;
     }
 }
@@ -901,20 +1060,105 @@ uint32_t next_tag() {
     return t;
 }
 
-template <int DT, int D, int B>
+template <int DT, int D, int B, bool APPEND>
 hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stream) {
+    using C = Cfg<DT, D, B>;
     const int groups = (plan.workers + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups == 0) return hipSuccess;
-    void* args[] = {const_cast<DecodeArgs*>(&a)};
+    DecodeArgs args_copy = a;
+    args_copy.attn_groups = groups;
+    int writer_groups = 0;
+    if (APPEND) {
+        constexpr int rows_per_wave = 64 / (D * C::kElt / 16);
+        const int waves = (a.num_seqs * a.num_kv_heads + rows_per_wave - 1) / rows_per_wave;
+        writer_groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+    }
+    void* args[] = {&args_copy};
     const size_t lds = sizeof(int32_t) * (2 * (size_t)a.num_seqs + 1);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, B>), dim3(groups),
-                           dim3(kGroupThreads), args, lds, stream);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, B, APPEND>),
+                           dim3(groups + writer_groups), dim3(kGroupThreads), args, lds, stream);
 }
 
-template <int DT>
+template <int DT, bool APPEND>
 hipError_t dispatch_decode(const DecodeArgs& a, const Plan& plan, int D, int B, hipStream_t stream) {
-    if (D == 64) return B == 16 ? launch_decode<DT, 64, 16>(a, plan, stream) : launch_decode<DT, 64, 32>(a, plan, stream);
-    return B == 16 ? launch_decode<DT, 128, 16>(a, plan, stream) : launch_decode<DT, 128, 32>(a, plan, stream);
+    if (D == 64)
+        return B == 16 ? launch_decode<DT, 64, 16, APPEND>(a, plan, stream)
+                       : launch_decode<DT, 64, 32, APPEND>(a, plan, stream);
+    return B == 16 ? launch_decode<DT, 128, 16, APPEND>(a, plan, stream)
+                   : launch_decode<DT, 128, 32, APPEND>(a, plan, stream);
+}
+
+// Shared by pa_decode_ex and pa_decode_append (k_new/v_new non-null: fused append).
+pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                        const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                        int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                        const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes, int32_t num_workers,
+                        bool append, pa_stream_t stream) {
+    pa_status_t st = check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache);
+    if (st != PA_OK) return st;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
+    if (num_seqs == 0) return PA_OK;  // nothing is touched, so empty tensors may pass null pointers
+    if (!q || !k_cache || !v_cache || !context_lens || !out) return PA_ERR_INVALID_ARG;
+    if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(context_lens, 4) || (block_tables && !aligned(block_tables, 4)))
+        return PA_ERR_INVALID_ARG;
+    if (append && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return PA_ERR_INVALID_ARG;
+    Plan plan;
+    st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, &plan);
+    if (st != PA_OK) return st;
+    if (plan.bytes > 0 && (workspace == nullptr || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
+        return PA_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    DecodeArgs a{};
+    a.q = static_cast<const uint8_t*>(q);
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.v_cache = static_cast<const uint8_t*>(v_cache);
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.out = static_cast<uint8_t*>(out);
+    a.arrivals = plan.per_segment ? nullptr : reinterpret_cast<unsigned long long*>(ws);
+    a.tag = next_tag();
+    a.part_lse = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_lse);
+    a.part_o = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_o);
+    a.k_new = static_cast<const uint8_t*>(k_new);
+    a.v_new = static_cast<const uint8_t*>(v_new);
+    a.k_cache_w = static_cast<uint8_t*>(k_cache);
+    a.v_cache_w = static_cast<uint8_t*>(v_cache);
+    a.scale_log2 = scale * kLog2e;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.group = num_q_heads / cache->num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = cache->num_blocks;
+    a.num_workers = plan.workers;
+    a.per_segment = plan.per_segment;
+
+    // LDS of one decode workgroup: lengths and prefix (dynamic) plus the merge areas (static).
+    int lds_max = 0;
+    st = lds_limit(&lds_max);
+    if (st != PA_OK) return st;
+    if (sizeof(int32_t) * (2 * (size_t)num_seqs + 1) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
+
+    hipStream_t sm = static_cast<hipStream_t>(stream);
+    const int D = cache->head_dim, B = cache->block_size;
+    hipError_t e;
+    switch (cache->dtype) {
+        case PA_F32:
+            e = append ? dispatch_decode<PA_F32, true>(a, plan, D, B, sm) : dispatch_decode<PA_F32, false>(a, plan, D, B, sm);
+            break;
+        case PA_F16:
+            e = append ? dispatch_decode<PA_F16, true>(a, plan, D, B, sm) : dispatch_decode<PA_F16, false>(a, plan, D, B, sm);
+            break;
+        default:
+            e = append ? dispatch_decode<PA_BF16, true>(a, plan, D, B, sm)
+                       : dispatch_decode<PA_BF16, false>(a, plan, D, B, sm);
+            break;
+    }
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 }  // namespace
@@ -983,64 +1227,18 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
                          const int32_t* context_lens, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                          int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
                          size_t workspace_bytes, int32_t num_workers, pa_stream_t stream) {
-    pa_status_t st = check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache);
-    if (st != PA_OK) return st;
-    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
-    if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
-    if (num_seqs == 0) return PA_OK;  // nothing is touched, so empty tensors may pass null pointers
-    if (!q || !k_cache || !v_cache || !context_lens || !out) return PA_ERR_INVALID_ARG;
-    if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
-    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(context_lens, 4) || (block_tables && !aligned(block_tables, 4)))
-        return PA_ERR_INVALID_ARG;
-    Plan plan;
-    st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, &plan);
-    if (st != PA_OK) return st;
-    if (plan.bytes > 0 && (workspace == nullptr || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
-        return PA_ERR_WORKSPACE;
+    return decode_impl(q, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_tables,
+                       context_lens, scale, out, num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace,
+                       workspace_bytes, num_workers, false, stream);
+}
 
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    DecodeArgs a{};
-    a.q = static_cast<const uint8_t*>(q);
-    a.k_cache = static_cast<const uint8_t*>(k_cache);
-    a.v_cache = static_cast<const uint8_t*>(v_cache);
-    a.block_tables = block_tables;
-    a.context_lens = context_lens;
-    a.out = static_cast<uint8_t*>(out);
-    a.arrivals = plan.per_segment ? nullptr : reinterpret_cast<unsigned long long*>(ws);
-    a.tag = next_tag();
-    a.part_lse = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_lse);
-    a.part_o = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_o);
-    a.scale_log2 = scale * kLog2e;
-    a.num_seqs = num_seqs;
-    a.num_q_heads = num_q_heads;
-    a.num_kv_heads = cache->num_kv_heads;
-    a.group = num_q_heads / cache->num_kv_heads;
-    a.max_blocks = max_blocks_per_seq;
-    a.num_blocks = cache->num_blocks;
-    a.num_workers = plan.workers;
-    a.per_segment = plan.per_segment;
-
-    // LDS of one decode workgroup: lengths and prefix (dynamic) plus the merge areas (static).
-    int lds_max = 0;
-    st = lds_limit(&lds_max);
-    if (st != PA_OK) return st;
-    if (sizeof(int32_t) * (2 * (size_t)num_seqs + 1) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    switch (cache->dtype) {
-        case PA_F32:
-            e = dispatch_decode<PA_F32>(a, plan, cache->head_dim, cache->block_size, s);
-            break;
-        case PA_F16:
-            e = dispatch_decode<PA_F16>(a, plan, cache->head_dim, cache->block_size, s);
-            break;
-        default:
-            e = dispatch_decode<PA_BF16>(a, plan, cache->head_dim, cache->block_size, s);
-            break;
-    }
-    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                             const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
+                             int32_t num_workers, pa_stream_t stream) {
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
+                       num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers, true, stream);
 }
 
 pa_status_t pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

@@ -46,6 +46,13 @@ class GpuCase:
         pa.write_kv(self.k_new, self.v_new, self.slot_new, self.k_cache, self.v_cache)
         self.appended = True
 
+    def decode_append(self, num_workers=0, out=None):
+        """The fused step: append the new tokens and attend, one launch."""
+        assert not self.appended
+        self.appended = True
+        return pa.decode_append(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache, self.bt, self.ctx,
+                                self.case.scale, out, num_workers=num_workers)
+
     def decode(self, num_workers=0, out=None):
         assert self.appended
         return pa.decode(self.q, self.k_cache, self.v_cache, self.bt, self.ctx, self.case.scale, out,

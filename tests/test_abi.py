@@ -99,6 +99,24 @@ def test_decode_rejects(kw, status):
     assert _decode(_desc(), **kw) == status
 
 
+def _append(desc, *, kn=A, vn=A, **kw):
+    base = dict(q=A, kc=A, vc=A, bt=A, ctx=A, out=A, S=2, Hq=4, maxblk=3, ws=A, ws_bytes=1 << 30, workers=64,
+                scale=0.125)
+    base.update(kw)
+    b = base
+    return pa.lib().pa_decode_append(b["q"], kn, vn, b["kc"], b["vc"], b["bt"], b["ctx"], b["scale"], b["out"],
+                                     b["S"], b["Hq"], b["maxblk"], ctypes.byref(desc), b["ws"], b["ws_bytes"],
+                                     b["workers"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), INVALID), (dict(vn=None), INVALID), (dict(kn=A + 8), INVALID), (dict(q=None), INVALID),
+    (dict(Hq=3), INVALID), (dict(ws=None), WORKSPACE), (dict(S=0, kn=None, vn=None), OK),
+])
+def test_decode_append_rejects(kw, status):
+    assert _append(_desc(), **kw) == status
+
+
 def test_decode_zero_sequences_is_a_noop():
     assert _decode(_desc(), S=0) == OK
 

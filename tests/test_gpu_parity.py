@@ -228,3 +228,42 @@ def test_graph_replay_matches_eager():
         # eager work on the same workspace between replays
         call()
         torch.cuda.synchronize()
+
+
+# ---- the fused step (pa_decode_append) against the two calls it replaces ----
+
+@pytest.mark.parametrize("workers", [0, -1, 37])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5])
+def test_decode_append_matches_write_then_decode(n, workers):
+    case, g, kp, vp, ref = config_state(n)
+    log(f"[fused] workload {n} workers={workers}")
+    f = GpuCase(case)  # prefill only; the step appends
+    out_f = f.decode_append(num_workers=workers)
+    out_s = g.decode(num_workers=workers)
+    torch.cuda.synchronize()
+    assert torch.equal(dev_bits(out_f), dev_bits(out_s))
+    assert torch.equal(dev_bits(f.k_cache), dev_bits(g.k_cache)) and torch.equal(dev_bits(f.v_cache),
+                                                                                 dev_bits(g.v_cache))
+    err = max_abs_err(out_f, ref)
+    log(f"[fused] workload {n} workers={workers}: max abs err {err:.3e}")
+    assert err <= TOL[case.dtype]
+    del f
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("workers", [0, -1, 3, 10000])
+@pytest.mark.parametrize("idx", range(len(SMALL)))
+def test_decode_append_small_shapes(idx, workers):
+    kw = dict(SMALL[idx])
+    case = W.make_case(seed=200 + idx, **kw)
+    log(f"[fused small] {idx} {kw} workers={workers}")
+    f = GpuCase(case)
+    out_f = f.decode_append(num_workers=workers)
+    g = GpuCase(case)
+    g.append()
+    out_s = g.decode(num_workers=workers)
+    torch.cuda.synchronize()
+    assert torch.equal(dev_bits(out_f), dev_bits(out_s))
+    kp, vp = oracle_pools(case)
+    assert torch.equal(flat_bits(f.k_cache), flat_bits(kp)) and torch.equal(flat_bits(f.v_cache), flat_bits(vp))
+    assert max_abs_err(out_f, oracle.decode_case(case, kp, vp)) <= TOL[case.dtype]

@@ -37,10 +37,10 @@ def k_row(c, k_pool, p, o):
 
 def v_row(c, v_pool, p, o):
     Y = 4 // c.elt
-    vv = v_pool.view(c.num_blocks, c.Hkv, c.B // 16, c.D // (16 * Y), 16, 4, Y, 4)
+    vv = v_pool.view(c.num_blocks, c.Hkv, c.B // 16, 4, c.D // (16 * Y), 16, Y, 4)
     d = torch.arange(c.D)
     t = o % 16
-    return vv[p, :, o // 16][:, d // (16 * Y), d % 16, t // 4, (d // 16) % Y, t % 4]
+    return vv[p, :, o // 16][:, t // 4, d // (16 * Y), d % 16, (d // 16) % Y, t % 4]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
