@@ -134,7 +134,7 @@ def measure(n, args, device):
     log(f"[bench] workload {n}: {layers} layers of {layer_bytes / 1e9:.2f} GB; timing {args.steps} steps")
     t_step, fused_ms = time_fused(steps, args.steps, args.warmup)
     t_write, t_decode, split_ms = time_two_calls(steps, args.steps, args.warmup)
-    dec_b, wr_b = W.decode_bytes(case), W.write_bytes(case)
+    dec_b, wr_b, st_b = W.decode_bytes(case), W.write_bytes(case), W.step_bytes(case)
     step_mean = statistics.fmean(t_step)
     dec_mean = statistics.fmean(t_decode)
     return dict(
@@ -145,7 +145,8 @@ def measure(n, args, device):
         # the fused step: pa_decode_append
         ms_per_step=fused_ms / args.steps,
         step_us=dict(mean=step_mean, p10=pct(t_step, 10), p50=pct(t_step, 50), p90=pct(t_step, 90)),
-        step_gbs=(dec_b + wr_b) / (step_mean * 1e-6) / 1e9,
+        step_bytes=st_b,
+        step_gbs=st_b / (step_mean * 1e-6) / 1e9,
         seq_heads_per_s=case.S * case.Hq / (step_mean * 1e-6),
         # the same step as two calls: pa_write_kv, then pa_decode
         two_call_ms_per_step=split_ms / args.steps,
@@ -197,7 +198,7 @@ def cpu_baseline(case, min_seconds):
         t_total += time.perf_counter() - t
         reps += 1
     per_step = t_total / reps
-    gbs = (W.decode_bytes(case) + W.write_bytes(case)) / per_step / 1e9
+    gbs = W.step_bytes(case) / per_step / 1e9
     return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
                 sample=f"the whole workload (append + decode of all {case.S} sequences), {reps} reps, "
                        f"{per_step * 1e3:.1f} ms per step, float64 C oracle")
@@ -257,7 +258,7 @@ def main():
             two_call_t_layer_us_p50=round(r["t_layer_us_p50"], 2),
             decode_gbs=round(r["decode_gbs"], 1), decode_frac_of_peak=round(r["decode_gbs"] / PEAK_HBM_GBS, 4),
             seq_heads_per_s=round(r["seq_heads_per_s"]), layers=r["layers"],
-            step_bytes=r["decode_bytes"] + r["write_bytes"], context_tokens=int(c.context_lens.sum()))
+            step_bytes=r["step_bytes"], context_tokens=int(c.context_lens.sum()))
         del c, r
         torch.cuda.empty_cache()
 
@@ -266,7 +267,7 @@ def main():
         log("[bench] timing the CPU oracle on the host")
         cpu = cpu_baseline(case, args.cpu_seconds)
 
-    step_bytes = main_res["decode_bytes"] + main_res["write_bytes"]
+    step_bytes = main_res["step_bytes"]
     line = {
         "metric": METRIC,
         "value": round(main_res["step_gbs"], 2),

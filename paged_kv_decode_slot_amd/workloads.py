@@ -291,6 +291,16 @@ def decode_bytes(case: Case) -> int:
     return kv + qo + bt + 4 * case.S
 
 
+def step_bytes(case: Case) -> int:
+    """Bytes one fused step (append, then decode) must move: the K and V rows of
+    the L - 1 cached positions of every sequence, its new token's rows read once
+    and stored once, q, out, the used block-table entries and the lengths."""
+    ctx = case.context_lens.astype(np.int64)
+    row = case.Hkv * case.D * case.elt * 2  # one position's K and V rows, all kv-heads
+    new = int((ctx > 0).sum())
+    return decode_bytes(case) - new * row + 2 * new * row
+
+
 def write_bytes(case: Case) -> int:
     """Bytes the KV-append of one new token per sequence must move (read + write of K and V, plus slots)."""
     T = case.S
