@@ -56,6 +56,10 @@ constexpr int kMaxGroup = 16;
 constexpr int kWorkersPerCU = PA_WORKERS_PER_CU;
 constexpr int kMinBlocksPerWorker = 16;
 constexpr int kMaxWorkers = 1 << 20;
+#ifndef PA_RUN_COST_BYTES
+#define PA_RUN_COST_BYTES 49152
+#endif
+constexpr size_t kRunCostBytes = PA_RUN_COST_BYTES;
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -224,6 +228,7 @@ struct DecodeArgs {
     int32_t num_workers;
     int32_t per_segment;  // 1: worker w owns (sequence, kv-head) w entirely
     int32_t attn_groups;  // append: workgroups [attn_groups, grid) store the new rows
+    int32_t run_cost;     // extra units counted per (sequence, kv-head) with context (see load_lengths)
 };
 
 __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
@@ -232,7 +237,10 @@ __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
 }
 
 // Context lengths (clamped) and the exclusive prefix over sequences of their
-// block counts, into LDS: ctx[S], pre[S + 1].
+// unit counts, into LDS: ctx[S], pre[S + 1].  A sequence with nb > 0 blocks
+// counts nb + run_cost units per kv-head: the work split deals out units, and
+// the first run_cost units of a pair stand for the cost of starting a run on
+// it (loading Q, waiting for the first tile) and hold no blocks.
 template <int B>
 __device__ void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, int32_t* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -243,7 +251,7 @@ __device__ void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, in
     for (int i = lo; i < hi; ++i) {
         const int c = clamp_ctx(a.context_lens[i], B, a.max_blocks);
         ctx[i] = c;
-        sum += (c + B - 1) / B;
+        sum += c > 0 ? (c + B - 1) / B + a.run_cost : 0;
     }
     int x = sum;
 #pragma unroll
@@ -257,7 +265,7 @@ __device__ void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, in
     for (int w = 0; w < wave; ++w) run += wave_tot[w];
     for (int i = lo; i < hi; ++i) {
         pre[i] = run;
-        run += (ctx[i] + B - 1) / B;
+        run += ctx[i] > 0 ? (ctx[i] + B - 1) / B + a.run_cost : 0;
     }
     if (tid == kGroupThreads - 1) pre[S] = run;
     __syncthreads();
@@ -297,7 +305,12 @@ __device__ inline float coherent_load(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // All of this wave's outstanding vector-memory operations (stores included) complete.
-__device__ inline void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt immediate for vmcnt(0) alone (expcnt 7 and lgkmcnt 15 wait for
+// nothing).  Issued through the builtin, the compiler sees the wait and knows
+// that no vector-memory access is outstanding after it.
+constexpr int kWaitVmcnt0 = 0x0F70;
+__device__ inline void wait_vmem_done() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); }
+__device__ inline void wait_stores_done() { wait_vmem_done(); }
 
 // Count this wave's part of a split (sequence, kv-head); true for the wave
 // that stores the last part.  The word holds (tag << 32) | parts counted; a
@@ -399,16 +412,13 @@ __device__ inline float row_group_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Per-wave LDS used by a merge: part weights and locations of up to 64 parts,
-// per-head running maximum, denominator and rescale factor, and the output
-// accumulators (pass p holds head p*HP + lane/LH, dims 2*(lane%LH) + {0,1}).
+// Per-wave LDS used by a merge: part weights of up to 64 parts, and the
+// per-head running maximum, denominator and rescale factor.
 struct MergeLds {
     float w[kWave][kMaxGroup];  // weight of part k for head h (relative to the running max)
-    int32_t loc[kWave];         // part_index(worker, slot, G, 0) of part k
     float M[kMaxGroup];         // running maximum of the parts' log-sum-exps (log2 domain)
     float den[kMaxGroup];       // running sum of weights
     float rescale[kMaxGroup];   // factor applied to earlier chunks when the running max grows
-    float2 acc[kMaxGroup][kWave];
 };
 
 // Lane x of the same 16-lane row, by DPP: quad_perm [1,0,3,2] (xor 1),
@@ -433,11 +443,6 @@ __device__ inline float wave_sum(float x) {
     x += dpp<0x128>(x);
     return row_group_sum(x);
 }
-__device__ inline float2 coherent_load2(const float* p) {
-    const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    return __builtin_bit_cast(float2, v);
-}
 
 // Combine the parts of a split (sequence, kv-head) by log-sum-exp and write out.
 // Parts are the workers whose runs cover units [F, F + nb): with W >= U each
@@ -447,39 +452,98 @@ __device__ inline float2 coherent_load2(const float* p) {
 // (the maximum and the weights follow by wave reductions); then the (pass,
 // part) items of the chunk are read kBatch at a time, each lane loading two
 // output dims of one head per item, and accumulated in LDS.
-template <int DT, int D>
-__device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int64_t F, int nb, int64_t U, int64_t W,
-                            MergeLds& L) {
-    constexpr int E = DT == PA_F32 ? 4 : 2;
-    constexpr int LH = D / 2;       // lanes per head: one pair of dims each
-    constexpr int HP = kWave / LH;  // heads per pass over the lanes
-    constexpr int kBatch = 32;      // item loads in flight per lane
-    const int lane = threadIdx.x & 63, G = a.group;
-    const bool unit_runs = W >= U;
-    const int64_t wa = owner_of(F, U, W);
-    const int parts = unit_runs ? nb : (int)(owner_of(F + nb - 1, U, W) - wa + 1);
-    const int first_slot = run_start(wa, U, W) == F ? 0 : 1;
-    const int pl = lane % LH, hs = lane / LH;
-    const int passes = (G + HP - 1) / HP;
+// Partial results read through buffer resources: loads are bounds-checked to
+// the resource (a load past its end returns 0) and carry the agent-coherence
+// bit (the cache-policy operand's SC1, 16), like the relaxed agent-scope loads
+// above.  Word 3 is the gfx9-family raw-buffer format.
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kCoherentPolicy = 16;
+__device__ inline f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kCoherentPolicy));
+}
+__device__ inline float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_offset) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_offset, 0, kCoherentPolicy));
+}
 
+// The log-sum-exp merge of a (sequence, kv-head) pair's parts, by the wave
+// that stored the last one.  The pair's G x D outputs are cut into 16-byte
+// units; in a pass over units [unit0, unit0 + 64 UPL), lane l owns units
+// unit0 + l + 64 i (i < UPL) and keeps their float4 accumulators in registers.  Parts are taken 64 at a time: the lanes read one
+// part's G log-sum-exps each, and per head the wave forms the running maximum
+// M, the weights 2^(lse - M) and their sum.  The outputs are read PB = 32/UPL
+// parts per batch, 32 16-byte loads in flight per lane; the first batch is
+// issued before the log-sum-exps, so a merge of up to PB parts costs one
+// round trip to memory.
+template <int DT, int D, int UPL>
+__device__ void merge_body(const DecodeArgs& a, int s, int kvh, int64_t F, int parts, int64_t wa, int first_slot,
+                           bool unit_runs, int64_t U, int64_t W, int unit0, MergeLds& L) {
+    constexpr int E = DT == PA_F32 ? 4 : 2;
+    constexpr int PB = 16 / UPL;
+    const int lane = threadIdx.x & 63, G = a.group;
+    const int NU = G * D / 4;
+    const int part_bytes = G * D * 4;
+    const int lse_bytes = (int)(W * 2 * G * 4);  // every worker's two slots of G log-sum-exps
+    const __amdgpu_buffer_rsrc_t lse_r =
+        __builtin_amdgcn_make_buffer_rsrc(a.part_lse, (short)0, lse_bytes, kBufferWord3);
+
+    f32x4 acc[UPL];
+    int hu[UPL];
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+        acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        hu[i] = min((unit0 + lane + kWave * i) * 4 / D, G - 1);
+    }
     if (lane < kMaxGroup) {
         L.M[lane] = -INFINITY;
         L.den[lane] = 0.f;
     }
-    for (int p = 0; p < passes; ++p) L.acc[p][lane] = float2{0.f, 0.f};
     __builtin_amdgcn_wave_barrier();
+
+    // Index of part k's first log-sum-exp (part_index(worker, slot, G, 0)).
+    auto part_loc = [&](int k) -> int64_t {
+        const int64_t wk = unit_runs ? owner_of(F + k, U, W) : wa + k;
+        return (int64_t)part_index(wk, k == 0 ? first_slot : 0, G, 0);
+    };
+    // Every slot of v is defined and read on every path (unused slots are zero
+    // and weigh 0), so no load of the merge can be left pending where the
+    // next run reuses its register.
+    f32x4 v[PB][UPL];
+    auto issue = [&](int kb, int n) {  // parts kb .. kb + n - 1 (n <= PB), uniform
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) v[p][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (p < n) {
+                const float* base = a.part_o + part_loc(kb + p) * D;
+                const __amdgpu_buffer_rsrc_t r =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, part_bytes, kBufferWord3);
+#pragma unroll
+                for (int i = 0; i < UPL; ++i) v[p][i] = coherent_load4(r, (unit0 + lane + kWave * i) * 16);
+            }
+        }
+    };
+    auto consume = [&](int kb, int n, int k0) {
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+#pragma unroll
+            for (int i = 0; i < UPL; ++i) acc[i] += (p < n ? L.w[kb + p - k0][hu[i]] : 0.f) * v[p][i];
+        }
+    };
 
     for (int k0 = 0; k0 < parts; k0 += kWave) {
         const int cnt = min(kWave, parts - k0);
-        // Phase 1: lane k reads part k0 + k's log-sum-exps.
-        const int k = k0 + lane;
+        issue(k0, min(PB, cnt));
+        // Lane k reads part k0 + k's log-sum-exps.  The loads are not under a
+        // lane mask (a lane without a part reads past the end and gets 0), so
+        // the compiler sees every one of them consumed.
         const bool has = lane < cnt;
-        const int64_t wk = !has ? 0 : (unit_runs ? owner_of(F + k, U, W) : wa + k);
-        const int loc = has ? (int)part_index(wk, k == 0 ? first_slot : 0, G, 0) : 0;
+        const int lse_off = has ? (int)(part_loc(k0 + lane) * 4) : lse_bytes;
         float l[kMaxGroup];
 #pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) l[h] = (has && h < G) ? coherent_load(a.part_lse + loc + h) : -INFINITY;
-        L.loc[lane] = loc;
+        for (int h = 0; h < kMaxGroup; ++h) {
+            const float x = coherent_load1(lse_r, lse_off + 4 * h);
+            l[h] = (has && h < G) ? x : -INFINITY;
+        }
         for (int h = 0; h < G; ++h) {
             float lh = l[0];
 #pragma unroll
@@ -499,40 +563,51 @@ __device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int64_t F, int 
             }
             __builtin_amdgcn_wave_barrier();
         }
-        // Phase 2: item (p, kk) adds part kk's dims 2pl, 2pl+1 of head p*HP + hs.
-        for (int p = 0; p < passes; ++p) L.acc[p][lane] *= L.rescale[min(p * HP + hs, G - 1)];
-        const int items = passes * cnt;
-        for (int i0 = 0; i0 < items; i0 += kBatch) {
-            float2 v[kBatch];
+        if (k0 > 0) {
 #pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int it = i0 + b;
-                if (it < items) {
-                    const int p = it / cnt, kk = it - p * cnt;
-                    const int hh = min(p * HP + hs, G - 1);
-                    v[b] = coherent_load2(a.part_o + ((size_t)L.loc[kk] + hh) * D + 2 * pl);
-                }
-            }
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int it = i0 + b;
-                if (it < items) {
-                    const int p = it / cnt, kk = it - p * cnt;
-                    const int hh = min(p * HP + hs, G - 1);
-                    L.acc[p][lane] += L.w[kk][hh] * v[b];
-                }
-            }
+            for (int i = 0; i < UPL; ++i) acc[i] *= L.rescale[hu[i]];
+        }
+        consume(k0, min(PB, cnt), k0);
+        for (int kb = k0 + PB; kb < k0 + cnt; kb += PB) {
+            const int n = min(PB, k0 + cnt - kb);
+            issue(kb, n);
+            consume(kb, n, k0);
         }
         __builtin_amdgcn_wave_barrier();
     }
-    for (int p = 0; p < passes; ++p) {
-        const int h = p * HP + hs;
-        if (h < G) {
-            uint8_t* dst = a.out + (((size_t)s * a.num_q_heads + kvh * G + h) * D + 2 * pl) * E;
-            store2<DT>(dst, L.acc[p][lane] * (1.f / L.den[h]));
+    // Every load above has been consumed by now; saying so (vmcnt 0, before
+    // the stores) keeps the compiler from draining the next run's loads at its
+    // start for a load it cannot prove done.
+    wait_vmem_done();
+#pragma unroll
+    for (int i = 0; i < UPL; ++i) {
+        const int u = unit0 + lane + kWave * i;
+        if (u < NU) {
+            const int h = u * 4 / D, d = u * 4 % D;
+            uint8_t* dst = a.out + (((size_t)s * a.num_q_heads + kvh * G + h) * D + d) * E;
+            store4<DT>(dst, acc[i] * (1.f / L.den[h]));
         }
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+template <int DT, int D>
+__device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int64_t F, int64_t Fv, int nb, int64_t U, int64_t W,
+                            MergeLds& L) {
+    const bool unit_runs = W >= U;
+    const int64_t wa = owner_of(F, U, W);
+    const int parts = unit_runs ? nb : (int)(owner_of(F + nb - 1, U, W) - wa + 1);
+    // The owner of the first block used slot 0 if this pair was its first run,
+    // i.e. its units begin at or after the pair's first unit Fv.
+    const int first_slot = run_start(wa, U, W) >= Fv ? 0 : 1;
+    const int units = a.group * D / 4;  // 16-byte output units of the pair
+    if (units <= kWave)
+        merge_body<DT, D, 1>(a, s, kvh, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+    else if (units <= 2 * kWave)
+        merge_body<DT, D, 2>(a, s, kvh, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+    else
+        for (int u0 = 0; u0 < units; u0 += 4 * kWave)  // up to 256 units per pass
+            merge_body<DT, D, 4>(a, s, kvh, F, parts, wa, first_slot, unit_runs, U, W, u0, L);
 }
 
 // Attend query group (s, kvh) over logical blocks [j0, j1) of sequence s, whose
@@ -541,7 +616,7 @@ __device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int64_t F, int 
 // and the wave that stores the pair's last partial merges them.
 template <int DT, int D, int B, bool APPEND>
 __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0, int j1, int nb, int64_t F,
-                           int64_t U, int64_t W, int w, int slot, MergeLds& mlds) {
+                           int64_t Fv, int64_t U, int64_t W, int w, int slot, MergeLds& mlds) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
     constexpr int NBUF = PA_TILE_BUFFERS;
@@ -723,6 +798,11 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
         }
     }
 
+    // Every tile load has been consumed; saying so before the stores below keeps
+    // the compiler from draining the next run's first loads for a load it
+    // cannot prove done (a register it would overwrite).
+    wait_vmem_done();
+
     // Full denominator of the lane's head: the four row groups hold disjoint tokens.
     lsum = row_group_sum(lsum);
     const float inv = 1.f / lsum;
@@ -749,7 +829,7 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     const int parts = W >= U ? nb : (int)(owner_of(F + nb - 1, U, W) - owner_of(F, U, W) + 1);
     int last = 0;
     if (lane == 0) last = arrive(a.arrivals + (size_t)s * a.num_kv_heads + kvh, a.tag, parts) ? 1 : 0;
-    if (__shfl(last, 0)) merge_parts<DT, D>(a, s, kvh, F, nb, U, W, mlds);
+    if (__shfl(last, 0)) merge_parts<DT, D>(a, s, kvh, F, Fv, nb, U, W, mlds);
 }
 
 // Fused append, the store side: wave `wi` of the writer workgroups copies the
@@ -865,7 +945,7 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
             reinterpret_cast<uint4*>(orow)[i] = make_uint4(0, 0, 0, 0);
     }
 
-    const int64_t U = (int64_t)s_pre[S] * Hkv;
+    const int64_t U = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[S]) * Hkv;  // uniform: a scalar loop
     int64_t start, end;
     if (a.per_segment) {
         if (w >= S * Hkv) return;
@@ -881,16 +961,20 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         // Every lane holds the same values; readfirstlane lets them live in scalar registers.
         const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, (int)(u / Hkv)));
         const int base = __builtin_amdgcn_readfirstlane(s_pre[s]);
-        const int nb = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - base;
+        const int nbv = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - base;  // units of each pair
         const int ctx = __builtin_amdgcn_readfirstlane(s_ctx[s]);
+        const int nb = (ctx + B - 1) / B;  // its blocks
+        const int cost = nbv - nb;         // its leading units that hold no block
         const int off = (int)(u - (int64_t)base * Hkv);
-        const int kvh = off / nb, j0 = off % nb;
+        const int kvh = off / nbv, jv0 = off % nbv;
         const int64_t left = end - u;
-        const int j1 = left < (int64_t)(nb - j0) ? j0 + (int)left : nb;
-        const int64_t F = (int64_t)base * Hkv + (int64_t)kvh * nb;
-        attend_run<DT, D, B, APPEND>(a, s, kvh, ctx, j0, j1, nb, F, U, W, w, u == start ? 0 : 1,
-                                     s_merge[threadIdx.x >> 6]);
-        u += j1 - j0;
+        const int jv1 = left < (int64_t)(nbv - jv0) ? jv0 + (int)left : nbv;
+        const int j0 = jv0 > cost ? jv0 - cost : 0, j1 = jv1 - cost;
+        const int64_t Fv = (int64_t)base * Hkv + (int64_t)kvh * nbv;  // the pair's first unit
+        if (j1 > j0)  // a range that ends inside the leading units holds no block
+            attend_run<DT, D, B, APPEND>(a, s, kvh, ctx, j0, j1, nb, Fv + cost, Fv, U, W, w, u == start ? 0 : 1,
+                                         s_merge[threadIdx.x >> 6]);
+        u += jv1 - jv0;
     }
 }
 
@@ -1136,6 +1220,10 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     a.num_blocks = cache->num_blocks;
     a.num_workers = plan.workers;
     a.per_segment = plan.per_segment;
+    // A run start costs about as much as streaming kRunCostBytes of K/V: count
+    // it as that many units so that workers with many short runs get fewer blocks.
+    const size_t unit_bytes = (size_t)cache->block_size * cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2) * 2;
+    a.run_cost = plan.per_segment ? 0 : (int32_t)(kRunCostBytes / unit_bytes);
 
     // LDS of one decode workgroup: lengths and prefix (dynamic) plus the merge areas (static).
     int lds_max = 0;
