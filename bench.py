@@ -2,19 +2,23 @@
 """Decode-step benchmark on one MI355X.
 
 A step is one pass of the whole path over one batch: the KV append of one new
-token per sequence (pa_write_kv) followed by paged decode attention
-(pa_decode).  The default workload is the Llama-3-8B-shaped layer: 64
-sequences, 32 query / 8 kv heads, head_dim 128, block 16, bf16, context
-lengths uniform on [512, 4096], shuffled blocks (seed 3).
+token per sequence and paged decode attention, as one pa_decode_append launch.
+The default workload is the Llama-3-8B-shaped layer: 64 sequences, 32 query /
+8 kv heads, head_dim 128, block 16, bf16, context lengths uniform on
+[512, 4096], shuffled blocks (seed 3).
 
 Steps rotate over several "layers", each with its own K/V pools, so that the
 bytes a step reads are not left in the 256 MB last-level cache by the step
 before (as in a real model, where every layer has its own cache).  Inputs are
-resident in HBM before timing starts.
+resident in HBM before timing starts.  The timed region is K steps launched
+back to back on one stream between two HIP events, synchronized on both
+sides; per-launch event pairs (which add each launch's overhead) give the
+percentiles, and the same step as two calls (pa_write_kv, pa_decode_ex) is
+timed beside it.
 
 Prints one JSON line.  `value` is the algorithmic bytes of a step (K/V rows
-read, q read, out written, block-table entries and lengths, and the append's
-read+write) divided by the step time.
+of the cached positions, the new token's rows read and stored, q read, out
+written, block-table entries and lengths) divided by the step time.
 """
 from __future__ import annotations
 
@@ -75,46 +79,41 @@ def _events(n):
     return [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
 
 
-def time_two_calls(steps, n_steps, warmup):
-    """pa_write_kv then pa_decode per step; per-step events around each call."""
+def time_back_to_back(calls, n_steps, warmup):
+    """n_steps launches of calls[i % len(calls)] back to back between two events on the
+    launch stream, synchronized on both sides; returns the total in ms."""
     import torch
 
     for i in range(warmup):
-        w, d, _ = steps[i % len(steps)]
-        w()
-        d()
+        calls[i % len(calls)]()
     torch.cuda.synchronize()
-    ev = _events(n_steps)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
     for i in range(n_steps):
-        w, d, _ = steps[i % len(steps)]
-        ev[i][0].record()
-        w()
-        ev[i][1].record()
-        d()
-        ev[i][2].record()
+        calls[i % len(calls)]()
+    t1.record()
     torch.cuda.synchronize()
-    t_write = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_steps)]  # us
-    t_decode = [ev[i][1].elapsed_time(ev[i][2]) * 1e3 for i in range(n_steps)]
-    total_ms = ev[0][0].elapsed_time(ev[-1][2])
-    return t_write, t_decode, total_ms
+    return t0.elapsed_time(t1)
 
 
-def time_fused(steps, n_steps, warmup):
-    """pa_decode_append per step (the whole step in one launch); per-step events."""
+def time_each(calls, n_steps, warmup):
+    """Per-launch event pairs around each call of calls[i % len(calls)] (a list of
+    callables run in order per step); returns per-step lists of us, one per callable."""
     import torch
 
     for i in range(warmup):
-        steps[i % len(steps)][2]()
+        for c in calls[i % len(calls)]:
+            c()
     torch.cuda.synchronize()
-    ev = _events(n_steps)
+    k = len(calls[0])
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(k + 1)] for _ in range(n_steps)]
     for i in range(n_steps):
-        ev[i][0].record()
-        steps[i % len(steps)][2]()
-        ev[i][1].record()
+        for j, c in enumerate(calls[i % len(calls)]):
+            ev[i][j].record()
+            c()
+        ev[i][k].record()
     torch.cuda.synchronize()
-    t_step = [ev[i][0].elapsed_time(ev[i][1]) * 1e3 for i in range(n_steps)]
-    total_ms = ev[0][0].elapsed_time(ev[-1][1])
-    return t_step, total_ms
+    return [[ev[i][j].elapsed_time(ev[i][j + 1]) * 1e3 for i in range(n_steps)] for j in range(k)]
 
 
 def pct(xs, p):
@@ -131,29 +130,40 @@ def measure(n, args, device):
     layer_bytes = 2 * case.pool_numel * case.elt
     layers = args.layers or max(2, math.ceil(2 * 2**30 / layer_bytes))
     steps = setup_layers(case, layers, device, args.workers)
-    log(f"[bench] workload {n}: {layers} layers of {layer_bytes / 1e9:.2f} GB; timing {args.steps} steps")
-    t_step, fused_ms = time_fused(steps, args.steps, args.warmup)
-    t_write, t_decode, split_ms = time_two_calls(steps, args.steps, args.warmup)
+    K, Wm = args.steps, args.warmup
+    log(f"[bench] workload {n}: {layers} layers of {layer_bytes / 1e9:.2f} GB; timing {K} steps")
+    # The timed region: K fused steps back to back (the headline).
+    fused_ms = time_back_to_back([s[2] for s in steps], K, Wm)
+    # Beside it: the decode alone and the two-call step, back to back, and
+    # per-launch event pairs for percentiles (these include each launch's overhead).
+    decode_ms = time_back_to_back([s[1] for s in steps], K, Wm)
+    pairs = [(lambda w=w, d=d: (w(), d())) for (w, d, _) in steps]
+    two_ms = time_back_to_back(pairs, K, Wm)
+    (t_step,) = time_each([[s[2]] for s in steps], K, Wm)
+    t_write, t_decode = time_each([[s[0], s[1]] for s in steps], K, Wm)
     dec_b, wr_b, st_b = W.decode_bytes(case), W.write_bytes(case), W.step_bytes(case)
-    step_mean = statistics.fmean(t_step)
-    dec_mean = statistics.fmean(t_decode)
+    step_us = fused_ms * 1e3 / K
+    dec_us = decode_ms * 1e3 / K
     return dict(
         case=case,
         layers=layers,
         decode_bytes=dec_b,
         write_bytes=wr_b,
-        # the fused step: pa_decode_append
-        ms_per_step=fused_ms / args.steps,
-        step_us=dict(mean=step_mean, p10=pct(t_step, 10), p50=pct(t_step, 50), p90=pct(t_step, 90)),
         step_bytes=st_b,
-        step_gbs=st_b / (step_mean * 1e-6) / 1e9,
-        seq_heads_per_s=case.S * case.Hq / (step_mean * 1e-6),
-        # the same step as two calls: pa_write_kv, then pa_decode
-        two_call_ms_per_step=split_ms / args.steps,
-        t_decode_us=dict(mean=dec_mean, p10=pct(t_decode, 10), p50=pct(t_decode, 50), p90=pct(t_decode, 90)),
-        t_write_us=dict(mean=statistics.fmean(t_write), p50=pct(t_write, 50)),
-        t_layer_us_p50=pct([a + b for a, b in zip(t_write, t_decode)], 50),
-        decode_gbs=dec_b / (dec_mean * 1e-6) / 1e9,
+        # the fused step, pa_decode_append, back to back
+        ms_per_step=fused_ms / K,
+        step_us_mean=step_us,
+        step_gbs=st_b / (step_us * 1e-6) / 1e9,
+        seq_heads_per_s=case.S * case.Hq / (step_us * 1e-6),
+        step_us_events=dict(mean=statistics.fmean(t_step), p10=pct(t_step, 10), p50=pct(t_step, 50),
+                            p90=pct(t_step, 90)),
+        # pa_decode_ex alone, and pa_write_kv + pa_decode_ex, back to back
+        decode_us_mean=dec_us,
+        decode_gbs=dec_b / (dec_us * 1e-6) / 1e9,
+        two_call_ms_per_step=two_ms / K,
+        t_decode_us_events=dict(mean=statistics.fmean(t_decode), p10=pct(t_decode, 10), p50=pct(t_decode, 50),
+                                p90=pct(t_decode, 90)),
+        t_write_us_events=dict(mean=statistics.fmean(t_write), p50=pct(t_write, 50)),
     )
 
 
@@ -252,11 +262,11 @@ def main():
         c = r.pop("case")
         other[f"C{n}"] = dict(
             workload=W.CONFIGS[n]["name"],
-            step_us_mean=round(r["step_us"]["mean"], 2), step_us_p50=round(r["step_us"]["p50"], 2),
-            step_gbs=round(r["step_gbs"], 1), step_frac_of_peak=round(r["step_gbs"] / PEAK_HBM_GBS, 4),
-            two_call_t_decode_us_mean=round(r["t_decode_us"]["mean"], 2),
-            two_call_t_layer_us_p50=round(r["t_layer_us_p50"], 2),
-            decode_gbs=round(r["decode_gbs"], 1), decode_frac_of_peak=round(r["decode_gbs"] / PEAK_HBM_GBS, 4),
+            step_us=round(r["step_us_mean"], 2), step_gbs=round(r["step_gbs"], 1),
+            step_frac_of_peak=round(r["step_gbs"] / PEAK_HBM_GBS, 4),
+            decode_us=round(r["decode_us_mean"], 2), decode_gbs=round(r["decode_gbs"], 1),
+            decode_frac_of_peak=round(r["decode_gbs"] / PEAK_HBM_GBS, 4),
+            two_call_us=round(r["two_call_ms_per_step"] * 1e3, 2),
             seq_heads_per_s=round(r["seq_heads_per_s"]), layers=r["layers"],
             step_bytes=r["step_bytes"], context_tokens=int(c.context_lens.sum()))
         del c, r
@@ -268,6 +278,7 @@ def main():
         cpu = cpu_baseline(case, args.cpu_seconds)
 
     step_bytes = main_res["step_bytes"]
+    r2 = lambda d: {k: round(v, 2) for k, v in d.items()}
     line = {
         "metric": METRIC,
         "value": round(main_res["step_gbs"], 2),
@@ -298,21 +309,24 @@ def main():
             "traffic": measured_traffic(args.config, "fused"),
             "traffic_unit": "bytes per launch",
             "bytes_per_launch": step_bytes,
-            "launch_us_mean": round(main_res["step_us"]["mean"], 2),
+            "launch_us_mean": round(main_res["step_us_mean"], 2),
+            "timing": "HIP events around the K back-to-back launches on the launch stream",
         },
         "cpu_baseline": cpu,
         "detail": {
-            "step_us": {k: round(v, 2) for k, v in main_res["step_us"].items()},
             "seq_heads_per_s": round(main_res["seq_heads_per_s"]),
             "step_bytes": step_bytes,
+            "step_us_per_launch_events": r2(main_res["step_us_events"]),
+            "decode_alone": {
+                "us": round(main_res["decode_us_mean"], 2),
+                "gbs": round(main_res["decode_gbs"], 1),
+                "frac_of_peak": round(main_res["decode_gbs"] / PEAK_HBM_GBS, 4),
+                "traffic": measured_traffic(args.config, "decode"),
+            },
             "two_calls": {
                 "ms_per_step": round(main_res["two_call_ms_per_step"], 5),
-                "t_write_us": {k: round(v, 2) for k, v in main_res["t_write_us"].items()},
-                "t_decode_us": {k: round(v, 2) for k, v in main_res["t_decode_us"].items()},
-                "t_layer_us_p50": round(main_res["t_layer_us_p50"], 2),
-                "decode_gbs": round(main_res["decode_gbs"], 1),
-                "decode_frac_of_peak": round(main_res["decode_gbs"] / PEAK_HBM_GBS, 4),
-                "decode_traffic": measured_traffic(args.config, "decode"),
+                "t_write_us_per_launch_events": r2(main_res["t_write_us_events"]),
+                "t_decode_us_per_launch_events": r2(main_res["t_decode_us_events"]),
             },
             "other": other,
         },
