@@ -1,4 +1,5 @@
-"""CPU oracle for paged-KV decode attention and the KV-append slot write.
+"""CPU oracle for paged-KV decode attention (one or several query tokens per
+sequence) and the KV-append slot write.
 
 TEST INFRASTRUCTURE: only the tests, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` use this package.  The HIP library never
@@ -45,6 +46,8 @@ def _load():
         lib.oracle_write_kv.restype = I
         lib.oracle_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, I, I, I, I, I, I, I, P, I64, I]
         lib.oracle_decode.restype = I
+        lib.oracle_attend.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I, I, I, I, I, I, I, I]
+        lib.oracle_attend.restype = I
         lib.oracle_widen.argtypes = [P, I64, I, P]
         lib.oracle_widen.restype = None
         _lib = lib
@@ -111,6 +114,27 @@ def decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_ta
                                _DTYPE_CODE[q.dtype], pp, npairs, threads or default_threads())
     if rc:
         raise ValueError("oracle_decode: bad argument")
+    return out
+
+
+def attend(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_tables: np.ndarray,
+           context_lens: np.ndarray, query_start: np.ndarray, scale: float, *, Hkv: int, B: int,
+           threads: int | None = None) -> np.ndarray:
+    """float64 causal attention of several query tokens per sequence: q is
+    [rows, Hq, D], sequence s owning rows query_start[s] .. query_start[s+1]-1
+    (its newest positions); returns [rows, Hq, D]."""
+    rows, Hq, D = q.shape
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    S = ctx.shape[0]
+    assert bt.shape[0] == S and qs.shape == (S + 1,) and int(qs[-1]) == rows
+    out = np.empty((rows, Hq, D), dtype=np.float64)
+    rc = _load().oracle_attend(_ptr(q.contiguous()), _ptr(k_pool), _ptr(v_pool), _ptr(bt), _ptr(ctx), _ptr(qs),
+                               float(np.float32(scale)), _ptr(out), S, Hq, Hkv, D, B, bt.shape[1],
+                               _DTYPE_CODE[q.dtype], threads or default_threads())
+    if rc:
+        raise ValueError("oracle_attend: bad argument")
     return out
 
 

@@ -27,6 +27,15 @@
  *    is the newest position, so the causal mask is exactly t < L).  All
  *    arithmetic is double; stored values are widened exactly.
  *
+ *  attend (several query tokens per sequence): the same sum for each of a
+ *    sequence's n newest positions, with the causal mask of a decoder
+ *    (ForgeLLM README, feature list: causal masking; the paragraph under the
+ *    architecture flowchart: long prompts are split into bounded chunks and
+ *    interleaved with decode; TokenForge post: speculative decoding, whose
+ *    draft tokens are checked by exactly this attention).  Query token i of
+ *    sequence s sits at position L - n + i and sees positions t <= L - n + i,
+ *    so it is the decode sum over the first L - n + i + 1 positions.
+ *
  * Pool layout.  The pages fix none; this is the layout documented for the
  * library's caller.  A block keeps its tokens in slabs of 16 consecutive
  * tokens (B a multiple of 16); each (block, kv-head, slab) holds 16 * D
@@ -128,17 +137,22 @@ typedef struct {
     int S, Hq, Hkv, D, B, maxblk, dtype;
     const int32_t* pairs; /* (s, h) pairs to compute, or NULL for all */
     int64_t npairs;
-    double* out; /* [npairs][D] */
+    const int32_t* qstart;  /* several query tokens per sequence: [S + 1], else NULL */
+    const int32_t* row_seq; /* with qstart: the sequence of each query row */
+    double* out;            /* [npairs][D], [S][Hq][D], or [query rows][Hq][D] */
     int64_t first, last;
     int status;
 } job_t;
 
-/* One (s, h): the definition written out. */
-static int attend_one(const job_t* J, int s, int h, double* out_row) {
+/*
+ * One output row: query row qrow (of q's [rows][Hq][D]), head h, over the
+ * first L positions of sequence s, gathered through its block table.  The
+ * definition written out.
+ */
+static int attend_one(const job_t* J, int s, int qrow, int h, int L, double* out_row) {
     int G = J->Hq / J->Hkv;
     int g = h / G;
     int X = 16 / elt_bytes(J->dtype), Y = 4 / elt_bytes(J->dtype);
-    int L = J->ctx[s];
     int D = J->D;
     if (L < 0 || L > J->maxblk * J->B) return -1;
     for (int d = 0; d < D; ++d) out_row[d] = 0.0;
@@ -151,7 +165,7 @@ static int attend_one(const job_t* J, int s, int h, double* out_row) {
         free(z);
         return -1;
     }
-    for (int d = 0; d < D; ++d) q[d] = widen(J->q, ((size_t)s * J->Hq + h) * D + d, J->dtype);
+    for (int d = 0; d < D; ++d) q[d] = widen(J->q, ((size_t)qrow * J->Hq + h) * D + d, J->dtype);
 
     /* logits through the block table */
     for (int t = 0; t < L; ++t) {
@@ -182,15 +196,36 @@ static int attend_one(const job_t* J, int s, int h, double* out_row) {
 static void* run_job(void* arg) {
     job_t* J = (job_t*)arg;
     for (int64_t k = J->first; k < J->last; ++k) {
-        int s, h;
-        if (J->pairs) {
-            s = J->pairs[2 * k];
-            h = J->pairs[2 * k + 1];
-        } else {
-            s = (int)(k / J->Hq);
+        int s, h, qrow, L;
+        if (J->qstart) {
+            /* query row qrow is token i of sequence s: position ctx - n + i, so it
+               sees the first ctx - n + i + 1 positions (causal) */
+            qrow = (int)(k / J->Hq);
             h = (int)(k % J->Hq);
+            s = J->row_seq[qrow];
+            int n = J->qstart[s + 1] - J->qstart[s];
+            int i = qrow - J->qstart[s];
+            L = J->ctx[s] - n + i + 1;
+            if (n > J->ctx[s]) {
+                J->status = -1;
+                return NULL;
+            }
+        } else {
+            if (J->pairs) {
+                s = J->pairs[2 * k];
+                h = J->pairs[2 * k + 1];
+            } else {
+                s = (int)(k / J->Hq);
+                h = (int)(k % J->Hq);
+            }
+            if (s < 0 || s >= J->S) {
+                J->status = -1;
+                return NULL;
+            }
+            qrow = s;
+            L = J->ctx[s];
         }
-        if (s < 0 || s >= J->S || h < 0 || h >= J->Hq || attend_one(J, s, h, J->out + (size_t)k * J->D)) {
+        if (h < 0 || h >= J->Hq || attend_one(J, s, qrow, h, L, J->out + (size_t)k * J->D)) {
             J->status = -1;
             return NULL;
         }
@@ -198,17 +233,7 @@ static void* run_job(void* arg) {
     return NULL;
 }
 
-/*
- * out: double [npairs][D] for the listed (s, h) pairs (pairs = int32 [npairs][2]),
- * or [S][Hq][D] when pairs is NULL (npairs ignored).  Work is split over
- * nthreads threads by (s, h); each output row is computed by one thread in the
- * fixed order above, so the result does not depend on nthreads.
- */
-int oracle_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
-                  const int32_t* context_lens, float scale, double* out, int S, int Hq, int Hkv, int D, int B,
-                  int max_blocks_per_seq, int dtype, const int32_t* pairs, int64_t npairs, int nthreads) {
-    if (Hkv <= 0 || Hq % Hkv || !layout_ok(B, D, dtype)) return -1;
-    int64_t n = pairs ? npairs : (int64_t)S * Hq;
+static int run_jobs(job_t proto, int64_t n, int nthreads) {
     if (nthreads < 1) nthreads = 1;
     if (nthreads > n) nthreads = n > 0 ? (int)n : 1;
     job_t* jobs = calloc((size_t)nthreads, sizeof(job_t));
@@ -219,25 +244,10 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, const i
         return -1;
     }
     for (int i = 0; i < nthreads; ++i) {
-        job_t* J = &jobs[i];
-        J->q = q;
-        J->k_pool = k_pool;
-        J->v_pool = v_pool;
-        J->bt = block_tables;
-        J->ctx = context_lens;
-        J->scale = (double)scale;
-        J->S = S;
-        J->Hq = Hq;
-        J->Hkv = Hkv;
-        J->D = D;
-        J->B = B;
-        J->maxblk = max_blocks_per_seq;
-        J->dtype = dtype;
-        J->pairs = pairs;
-        J->npairs = npairs;
-        J->out = out;
-        J->first = n * i / nthreads;
-        J->last = n * (i + 1) / nthreads;
+        jobs[i] = proto;
+        jobs[i].first = n * i / nthreads;
+        jobs[i].last = n * (i + 1) / nthreads;
+        jobs[i].status = 0;
     }
     int started = 0;
     for (int i = 1; i < nthreads; ++i) {
@@ -257,6 +267,80 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, const i
     }
     free(jobs);
     free(th);
+    return status;
+}
+
+/*
+ * Decode: one query token per sequence.  out: double [npairs][D] for the
+ * listed (s, h) pairs (pairs = int32 [npairs][2]), or [S][Hq][D] when pairs is
+ * NULL (npairs ignored).  Work is split over nthreads threads by output row;
+ * each row is computed by one thread in the fixed order above, so the result
+ * does not depend on nthreads.
+ */
+int oracle_decode(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                  const int32_t* context_lens, float scale, double* out, int S, int Hq, int Hkv, int D, int B,
+                  int max_blocks_per_seq, int dtype, const int32_t* pairs, int64_t npairs, int nthreads) {
+    if (Hkv <= 0 || Hq % Hkv || !layout_ok(B, D, dtype)) return -1;
+    job_t J;
+    memset(&J, 0, sizeof(J));
+    J.q = q;
+    J.k_pool = k_pool;
+    J.v_pool = v_pool;
+    J.bt = block_tables;
+    J.ctx = context_lens;
+    J.scale = (double)scale;
+    J.S = S;
+    J.Hq = Hq;
+    J.Hkv = Hkv;
+    J.D = D;
+    J.B = B;
+    J.maxblk = max_blocks_per_seq;
+    J.dtype = dtype;
+    J.pairs = pairs;
+    J.npairs = npairs;
+    J.out = out;
+    return run_jobs(J, pairs ? npairs : (int64_t)S * Hq, nthreads);
+}
+
+/*
+ * Several query tokens per sequence (the causal extension of decode: chunked
+ * prefill, speculative verification).  Sequence s owns query rows
+ * [query_start[s], query_start[s + 1]) of q ([rows][Hq][D]); they are its
+ * newest n = query_start[s+1] - query_start[s] positions of context_lens[s],
+ * and row i sees positions t <= context_lens[s] - n + i.  out: double
+ * [rows][Hq][D].  -1 on a bad argument (n > context_lens[s] included).
+ */
+int oracle_attend(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_tables,
+                  const int32_t* context_lens, const int32_t* query_start, float scale, double* out, int S, int Hq,
+                  int Hkv, int D, int B, int max_blocks_per_seq, int dtype, int nthreads) {
+    if (Hkv <= 0 || Hq % Hkv || !layout_ok(B, D, dtype) || query_start[0] != 0) return -1;
+    for (int s = 0; s < S; ++s)
+        if (query_start[s + 1] < query_start[s]) return -1;
+    int rows = query_start[S];
+    int32_t* row_seq = malloc(sizeof(int32_t) * (size_t)(rows > 0 ? rows : 1));
+    if (!row_seq) return -1;
+    for (int s = 0; s < S; ++s)
+        for (int r = query_start[s]; r < query_start[s + 1]; ++r) row_seq[r] = s;
+    job_t J;
+    memset(&J, 0, sizeof(J));
+    J.q = q;
+    J.k_pool = k_pool;
+    J.v_pool = v_pool;
+    J.bt = block_tables;
+    J.ctx = context_lens;
+    J.scale = (double)scale;
+    J.S = S;
+    J.Hq = Hq;
+    J.Hkv = Hkv;
+    J.D = D;
+    J.B = B;
+    J.maxblk = max_blocks_per_seq;
+    J.dtype = dtype;
+    J.qstart = query_start;
+    J.row_seq = row_seq;
+    J.out = out;
+    int status = run_jobs(J, (int64_t)rows * Hq, nthreads);
+    free(row_seq);
     return status;
 }
 

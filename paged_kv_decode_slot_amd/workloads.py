@@ -259,6 +259,52 @@ def make_case(*, S, Hq, Hkv, D, B, dtype, ctx=None, ctx_range=None, seed=0,
                 scale=float(np.float32(scale)), meta={"seed": seed, "pool": pool, "placement": placement})
 
 
+@dataclass
+class MultiCase:
+    """Several query tokens per sequence over the pools of ``base``: sequence s
+    owns query rows ``query_start[s] .. query_start[s+1]-1``, its newest
+    positions (their K/V are among the base case's written rows)."""
+
+    base: Case
+    q: torch.Tensor  # [rows, Hq, D]
+    query_start: np.ndarray  # int32 [S + 1]
+
+    @property
+    def q_lens(self) -> np.ndarray:
+        return np.diff(self.query_start)
+
+    @property
+    def max_q_len(self) -> int:
+        return int(self.q_lens.max()) if self.base.S else 0
+
+
+def with_queries(case: Case, q_lens, seed: int = 0) -> MultiCase:
+    """Query rows for ``case``'s sequences: ``q_lens[s]`` of them (clipped to the
+    context length), drawn as float32 standard normals rounded into the dtype
+    from their own generator (seeded with ``seed``)."""
+    n = np.minimum(np.asarray(q_lens, dtype=np.int64), case.context_lens.astype(np.int64))
+    n = np.maximum(n, 0)
+    assert n.shape == (case.S,)
+    rng = np.random.default_rng(seed)
+    q = _normal(rng, (int(n.sum()), case.Hq, case.D), case.dtype)
+    qs = np.zeros(case.S + 1, dtype=np.int32)
+    qs[1:] = np.cumsum(n)
+    return MultiCase(base=case, q=q, query_start=qs)
+
+
+def attend_bytes(mc: MultiCase) -> int:
+    """Bytes a multi-query attention call must move: every used K and V row once,
+    q read and out written, used block-table entries, lengths and query starts."""
+    case = mc.base
+    ctx = case.context_lens.astype(np.int64)
+    used = mc.q_lens > 0
+    kv = int(ctx[used].sum()) * case.Hkv * case.D * case.elt * 2
+    rows = int(mc.query_start[-1])
+    qo = 2 * rows * case.Hq * case.D * case.elt
+    bt = 4 * int(((ctx[used] + case.B - 1) // case.B).sum())
+    return kv + qo + bt + 4 * case.S + 4 * (case.S + 1)
+
+
 # The five workloads.  C1 is the small case the oracle finishes at once;
 # C3 and C4 are the Llama-3-8B-shaped ragged batches.
 CONFIGS = {

@@ -337,3 +337,105 @@ def test_seeded_context_lengths():
     c2 = W.make_case(seed=2, **{k: v for k, v in W.CONFIGS[2].items()})
     assert list(c2.context_lens) == [1736, 630, 337, 701, 922, 1692, 994, 304]
     assert c2.num_blocks - 1 == 577 and int(((c2.context_lens + 15) // 16).sum()) == 461
+
+
+# --- Several query tokens per sequence (causal): the oracle's attend ---
+
+def _attend(mc, threads=None):
+    k_pool, v_pool = oracle.build_pools(mc.base)
+    c = mc.base
+    return oracle.attend(mc.q, k_pool, v_pool, c.block_tables, c.context_lens, mc.query_start, c.scale,
+                         Hkv=c.Hkv, B=c.B, threads=threads)
+
+
+def test_attend_with_one_token_per_sequence_is_decode():
+    c = _case(S=4, Hq=8, Hkv=2, D=64, B=16, dtype="bf16", ctx_range=(1, 90), seed=31)
+    mc = W.MultiCase(base=c, q=c.q.clone(), query_start=np.arange(c.S + 1, dtype=np.int32))
+    assert np.array_equal(_attend(mc), oracle.decode_case(c))
+
+
+@pytest.mark.parametrize("kw,q_lens", [
+    (dict(S=3, Hq=4, Hkv=2, D=64, B=16, dtype="f32", ctx_range=(20, 70), seed=41), [1, 5, 20]),
+    (dict(S=4, Hq=8, Hkv=2, D=128, B=32, dtype="bf16", ctx_range=(1, 90), seed=42), [4, 4, 4, 4]),
+    (dict(S=3, Hq=7, Hkv=1, D=64, B=16, dtype="f16", ctx_range=(30, 50), seed=43), [0, 7, 30]),
+    (dict(S=2, Hq=16, Hkv=1, D=128, B=16, dtype="bf16", ctx=[17, 33], ctx_range=None, seed=44), [17, 2]),
+    (dict(S=5, Hq=4, Hkv=4, D=64, B=32, dtype="f32", ctx_range=(1, 40), seed=45), [3, 1, 0, 9, 40]),
+])
+def test_attend_matches_dense_causal(kw, q_lens):
+    c = _case(**kw)
+    mc = W.with_queries(c, q_lens, seed=kw["seed"] + 100)
+    got = _attend(mc)
+    ref = dense.dense_multi(mc)
+    assert got.shape == ref.shape and np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_attend_row_is_decode_over_its_visible_prefix():
+    # Query token i of a sequence with n tokens and context L is the decode of
+    # the same sequence cut to length L - n + i + 1: the same block table, the
+    # query row moved into a one-token batch.
+    c = _case(S=3, Hq=8, Hkv=2, D=64, B=16, dtype="bf16", ctx_range=(10, 60), seed=51)
+    mc = W.with_queries(c, [6, 1, 10], seed=52)
+    got = _attend(mc)
+    k_pool, v_pool = oracle.build_pools(c)
+    qs = mc.query_start
+    for s in range(c.S):
+        n = int(qs[s + 1] - qs[s])
+        for i in range(n):
+            row = int(qs[s]) + i
+            cut = np.array([int(c.context_lens[s]) - n + i + 1], dtype=np.int32)
+            ref = oracle.decode(mc.q[row:row + 1], k_pool, v_pool, c.block_tables[s:s + 1], cut, c.scale,
+                                Hkv=c.Hkv, B=c.B)
+            assert np.array_equal(got[row], ref[0])
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 16), ("bf16", 32)])
+def test_attend_bruteforce_tiny(dtype, D):
+    c = _case(S=2, Hq=2, Hkv=1, D=D, B=16, dtype=dtype, ctx=[5, 3], ctx_range=None, seed=61)
+    mc = W.with_queries(c, [3, 2], seed=62)
+    got = _attend(mc)
+    qs = mc.query_start
+    for s in range(c.S):
+        k, v = c.logical_kv(s)
+        k = k.to(torch.float64).numpy()
+        v = v.to(torch.float64).numpy()
+        L, n = int(c.context_lens[s]), int(qs[s + 1] - qs[s])
+        for i in range(n):
+            row = int(qs[s]) + i
+            vis = L - n + i + 1
+            for h in range(c.Hq):
+                q = mc.q[row, h].to(torch.float64).numpy()
+                ref = np.array(_brute(q, k[:vis, h // c.G], v[:vis, h // c.G], c.scale))
+                assert np.allclose(got[row, h], ref, rtol=1e-14, atol=1e-15)
+
+
+def test_attend_zero_query_gives_mean_of_visible_prefix():
+    # Closed form: with q = 0 every visible key weighs the same, so query row i
+    # of a sequence returns the plain mean of V over positions 0 .. L - n + i.
+    c = _case(S=3, Hq=4, Hkv=2, D=64, B=16, dtype="f32", ctx_range=(12, 50), seed=71)
+    mc = W.with_queries(c, [12, 1, 5], seed=72)
+    mc.q.zero_()
+    got = _attend(mc)
+    qs = mc.query_start
+    for s in range(c.S):
+        _, v = c.logical_kv(s)
+        v = v.to(torch.float64).numpy()
+        L, n = int(c.context_lens[s]), int(qs[s + 1] - qs[s])
+        for i in range(n):
+            for h in range(c.Hq):
+                ref = v[:L - n + i + 1, h // c.G].mean(axis=0)
+                assert np.max(np.abs(got[int(qs[s]) + i, h] - ref)) <= 1e-13
+
+
+def test_attend_rejects_more_queries_than_context():
+    c = _case(S=2, Hq=4, Hkv=2, D=64, B=16, dtype="f32", ctx=[3, 5], ctx_range=None, seed=81)
+    q = torch.zeros((7, c.Hq, c.D), dtype=torch.float32)
+    k_pool, v_pool = oracle.build_pools(c)
+    with pytest.raises(ValueError):
+        oracle.attend(q, k_pool, v_pool, c.block_tables, c.context_lens, np.array([0, 4, 7], dtype=np.int32),
+                      c.scale, Hkv=c.Hkv, B=c.B)
+
+
+def test_attend_thread_count_does_not_change_bits():
+    c = _case(S=4, Hq=8, Hkv=2, D=64, B=16, dtype="f16", ctx_range=(5, 80), seed=91)
+    mc = W.with_queries(c, [3, 5, 1, 4], seed=92)
+    assert np.array_equal(_attend(mc, threads=1), _attend(mc, threads=7))
