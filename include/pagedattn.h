@@ -167,6 +167,40 @@ pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new
                              const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
                              int32_t num_workers, pa_stream_t stream);
 
+/*
+ * Attention of several query tokens per sequence over the paged cache: the
+ * causal extension of pa_decode, for prompts split into chunks that run
+ * alongside decode steps and for checking speculative draft tokens (ForgeLLM
+ * README: feature list, causal masking and chunked prefill; the paragraph
+ * under its architecture flowchart; TokenForge post: speculative decoding).
+ * Sequence s owns query rows query_start[s] .. query_start[s+1] - 1, its
+ * n = query_start[s+1] - query_start[s] newest positions: with
+ * L = context_lens[s], query token i (row query_start[s] + i) sits at position
+ * L - n + i and, for every head h (kv-head h / G),
+ *   out[row][h][:] = sum_{t <= L-n+i} softmax_t(scale * q[row][h][:] . K_t) * V_t
+ * The K/V of all L positions, the query tokens' own included, must already be
+ * in the cache (pa_write_kv).  n = 1 for every sequence is exactly pa_decode_ex.
+ *   q, out         : [query_start[num_seqs]][num_q_heads][head_dim], 16-byte aligned
+ *   query_start    : int32 [num_seqs + 1], device, non-decreasing from 0
+ *   max_query_len  : host value >= every n (0: nothing to do)
+ *   other arguments as in pa_decode_ex; the workspace must hold
+ *   pa_attend_workspace_bytes(...) bytes
+ * Query tokens are taken floor(16 / G) at a time (one launch per group of
+ * tokens, all on `stream`): a group reads the K/V its tokens see once, so
+ * n > floor(16 / G) re-reads a sequence's K/V once per group.
+ * Preconditions (unchecked): n <= L, and those of pa_decode.  A column whose
+ * tokens see no position (only possible when n > L) gives 0.
+ */
+pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_query_len,
+                      const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes, int32_t num_workers,
+                      pa_stream_t stream);
+
+/* Workspace bytes pa_attend needs for these shapes and num_workers (0 for arguments it rejects). */
+size_t pa_attend_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 const pa_cache_desc_t* cache, int32_t num_workers);
+
 /* Workspace bytes pa_decode_ex and pa_decode_append need for that num_workers. */
 size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                     const pa_cache_desc_t* cache, int32_t num_workers);

@@ -1,4 +1,5 @@
-"""Paged-KV decode attention and KV append on MI355X (gfx950).
+"""Paged-KV decode attention (one or several query tokens per sequence) and
+KV append on MI355X (gfx950).
 
 The computation lives in the HIP library ``libpagedattn.so`` (C ABI declared
 in ``include/pagedattn.h``); this package is its thin Python binding plus the
@@ -7,6 +8,7 @@ seeded workload generator used by the tests and the benchmark.
 from .binding import (  # noqa: F401
     CacheDesc,
     PagedAttnError,
+    attend,
     cache_desc,
     cache_shapes,
     decode,
@@ -14,6 +16,7 @@ from .binding import (  # noqa: F401
     lib,
     library_path,
     new_cache,
+    prepare_attend,
     prepare_decode,
     prepare_decode_append,
     prepare_write_kv,

@@ -25,6 +25,8 @@ EXPORTS = (
     "pa_decode",
     "pa_decode_ex",
     "pa_decode_append",
+    "pa_attend",
+    "pa_attend_workspace_bytes",
     "pa_decode_workspace_bytes",
     "pa_decode_workspace_bytes_ex",
     "pa_status_string",
@@ -68,6 +70,10 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_ex.restype = ctypes.c_int
         L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, I32, P]
         L.pa_decode_append.restype = ctypes.c_int
+        L.pa_attend.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, I32, DP, P, SZ, I32, P]
+        L.pa_attend.restype = ctypes.c_int
+        L.pa_attend_workspace_bytes.argtypes = [I32, I32, I32, DP, I32]
+        L.pa_attend_workspace_bytes.restype = SZ
         L.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, DP]
         L.pa_decode_workspace_bytes.restype = SZ
         L.pa_decode_workspace_bytes_ex.argtypes = [I32, I32, I32, DP, I32]
@@ -281,6 +287,67 @@ def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, conte
 
     def call():
         _check("pa_decode_append", fn(*args))
+        return keep[5]
+
+    return call
+
+
+def _attend_args(q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, scale, out,
+                 num_workers, workspace):
+    desc = cache_desc(k_cache, v_cache)
+    dev = _dev(q, k_cache, v_cache, block_tables, context_lens, query_start)
+    if q.dim() != 3 or q.shape[2] != desc.head_dim or q.dtype != k_cache.dtype or not q.is_contiguous():
+        raise ValueError("q must be contiguous [rows, Hq, D] in the cache dtype")
+    _rows, Hq, D = q.shape
+    S = int(context_lens.shape[0]) if context_lens.dim() == 1 else -1
+    if context_lens.dtype != torch.int32 or S < 0 or not context_lens.is_contiguous():
+        raise ValueError("context_lens must be contiguous int32 [S]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [S, max_blocks_per_seq]")
+    if query_start.dtype != torch.int32 or query_start.shape != (S + 1,) or not query_start.is_contiguous():
+        raise ValueError("query_start must be contiguous int32 [S + 1]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be contiguous and shaped like q")
+    maxblk = int(block_tables.shape[1])
+    need = int(lib().pa_attend_workspace_bytes(S, Hq, maxblk, ctypes.byref(desc), int(num_workers)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor on the same device")
+    args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
+            query_start.data_ptr(), ctypes.c_float(scale), out.data_ptr(), S, Hq, maxblk, int(max_query_len),
+            ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), int(num_workers), _stream(dev))
+    return dev, out, args, (q, k_cache, v_cache, block_tables, context_lens, out, workspace, desc, query_start)
+
+
+def attend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+           context_lens: torch.Tensor, query_start: torch.Tensor, max_query_len: int, scale: float,
+           out: torch.Tensor | None = None, *, num_workers: int = 0,
+           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal attention of several query tokens per sequence: q [rows, Hq, D], sequence s
+    owning rows query_start[s] .. query_start[s+1]-1 (its newest positions, already
+    written to the caches); returns out [rows, Hq, D].  max_query_len bounds every
+    sequence's token count (a host value)."""
+    dev, out, args, _keep = _attend_args(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                         max_query_len, scale, out, num_workers, workspace)
+    with torch.cuda.device(dev):
+        st = lib().pa_attend(*args)
+    _check("pa_attend", st)
+    return out
+
+
+def prepare_attend(q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, scale, out=None, *,
+                   num_workers=0, workspace=None):
+    """Validate once; return a no-argument callable issuing the same pa_attend."""
+    _dev_, out, args, keep = _attend_args(q, k_cache, v_cache, block_tables, context_lens, query_start,
+                                          max_query_len, scale, out, num_workers, workspace)
+    fn = lib().pa_attend
+
+    def call():
+        _check("pa_attend", fn(*args))
         return keep[5]
 
     return call

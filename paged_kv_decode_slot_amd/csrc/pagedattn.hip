@@ -229,7 +229,27 @@ struct DecodeArgs {
     int32_t per_segment;  // 1: worker w owns (sequence, kv-head) w entirely
     int32_t attn_groups;  // append: workgroups [attn_groups, grid) store the new rows
     int32_t run_cost;     // extra units counted per (sequence, kv-head) with context (see load_lengths)
+    int32_t cols;         // columns of a pair: G heads, or (several query tokens) tpc tokens x G heads
+    const int32_t* query_start;  // several query tokens: [num_seqs + 1] query rows of each sequence
+    int32_t chunk;        // several query tokens: this launch takes tokens [chunk*tpc, (chunk+1)*tpc) of each
+    int32_t tpc;          // several query tokens: tokens per pair (16 / G)
 };
+
+// What a decode_kernel instantiation computes: one query token per sequence,
+// the same with the KV append fused in, or several query tokens per sequence.
+enum { kModeDecode = 0, kModeAppend = 1, kModeMulti = 2 };
+
+// Element offset (in q or out) of column c of pair (s, kvh).  One token per
+// sequence: head kvh*G + c of row s.  Several: the pair holds query rows
+// row0 .. row0 + tpc - 1, column c being head kvh*G + c % G of row row0 + c / G.
+template <bool MQ>
+__device__ inline size_t col_offset(const DecodeArgs& a, int s, int kvh, int row0, int c, int D) {
+    const int G = a.group;
+    if constexpr (MQ)
+        return ((size_t)(row0 + c / G) * a.num_q_heads + kvh * G + c % G) * D;
+    else
+        return ((size_t)s * a.num_q_heads + kvh * G + c) * D;
+}
 
 __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
     ctx = ctx < 0 ? 0 : ctx;
@@ -241,15 +261,30 @@ __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
 // counts nb + run_cost units per kv-head: the work split deals out units, and
 // the first run_cost units of a pair stand for the cost of starting a run on
 // it (loading Q, waiting for the first tile) and hold no blocks.
-template <int B>
-__device__ void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, int32_t* wave_tot) {
+//
+// With several query tokens per sequence (MQ), this launch's pair of sequence
+// s holds its query tokens i in [i0, i0 + rows), i0 = chunk * tpc; they see
+// positions up to L - n + i0 + rows - 1, so the pair's context is
+// L - n + i0 + rows; row0[s] is the query row of token i0, rows[s] the count
+// (0: no work for s in this launch).
+template <int B, bool MQ>
+__device__ void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, int32_t* row0, int32_t* rows,
+                             int32_t* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = a.num_seqs;
     const int per = (S + kGroupThreads - 1) / kGroupThreads;
     const int lo = min(S, tid * per), hi = min(S, lo + per);
     int sum = 0;
     for (int i = lo; i < hi; ++i) {
-        const int c = clamp_ctx(a.context_lens[i], B, a.max_blocks);
+        int c = clamp_ctx(a.context_lens[i], B, a.max_blocks);
+        if constexpr (MQ) {
+            const int q0 = a.query_start[i], n = a.query_start[i + 1] - q0;
+            const int i0 = a.chunk * a.tpc;
+            const int nr = i0 < n ? min(a.tpc, n - i0) : 0;
+            c = nr > 0 ? max(0, min(c, c - n + i0 + nr)) : 0;
+            row0[i] = q0 + i0;
+            rows[i] = nr;
+        }
         ctx[i] = c;
         sum += c > 0 ? (c + B - 1) / B + a.run_cost : 0;
     }
@@ -465,24 +500,27 @@ __device__ inline float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_offset
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_offset, 0, kCoherentPolicy));
 }
 
-// The log-sum-exp merge of a (sequence, kv-head) pair's parts, by the wave
-// that stored the last one.  The pair's G x D outputs are cut into 16-byte
-// units; in a pass over units [unit0, unit0 + 64 UPL), lane l owns units
-// unit0 + l + 64 i (i < UPL) and keeps their float4 accumulators in registers.  Parts are taken 64 at a time: the lanes read one
-// part's G log-sum-exps each, and per head the wave forms the running maximum
-// M, the weights 2^(lse - M) and their sum.  The outputs are read PB = 32/UPL
-// parts per batch, 32 16-byte loads in flight per lane; the first batch is
-// issued before the log-sum-exps, so a merge of up to PB parts costs one
-// round trip to memory.
-template <int DT, int D, int UPL>
-__device__ void merge_body(const DecodeArgs& a, int s, int kvh, int64_t F, int parts, int64_t wa, int first_slot,
-                           bool unit_runs, int64_t U, int64_t W, int unit0, MergeLds& L) {
+// The log-sum-exp merge of a pair's parts, by the wave that stored the last
+// one.  A pair has NC = a.cols columns (heads, or query token x head); its
+// NC x D outputs are cut into 16-byte units; in a pass over units
+// [unit0, unit0 + 64 UPL), lane l owns units unit0 + l + 64 i (i < UPL) and
+// keeps their float4 accumulators in registers.  Parts are taken 64 at a
+// time: the lanes read one part's NC log-sum-exps each, and per column the
+// wave forms the running maximum M, the weights 2^(lse - M) and their sum.
+// The outputs are read PB = 16/UPL parts per batch, 16 16-byte loads in
+// flight per lane; the first batch is issued before the log-sum-exps, so a
+// merge of up to PB parts costs one round trip to memory.  Only the first
+// `active` columns are stored (the rest pad the last token group).
+template <int DT, int D, int UPL, bool MQ>
+__device__ void merge_body(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int parts,
+                           int64_t wa, int first_slot, bool unit_runs, int64_t U, int64_t W, int unit0,
+                           MergeLds& L) {
     constexpr int E = DT == PA_F32 ? 4 : 2;
     constexpr int PB = 16 / UPL;
-    const int lane = threadIdx.x & 63, G = a.group;
-    const int NU = G * D / 4;
-    const int part_bytes = G * D * 4;
-    const int lse_bytes = (int)(W * 2 * G * 4);  // every worker's two slots of G log-sum-exps
+    const int lane = threadIdx.x & 63, NC = a.cols;
+    const int NU = NC * D / 4;
+    const int part_bytes = NC * D * 4;
+    const int lse_bytes = (int)(W * 2 * NC * 4);  // every worker's two slots of NC log-sum-exps
     const __amdgpu_buffer_rsrc_t lse_r =
         __builtin_amdgcn_make_buffer_rsrc(a.part_lse, (short)0, lse_bytes, kBufferWord3);
 
@@ -491,7 +529,7 @@ __device__ void merge_body(const DecodeArgs& a, int s, int kvh, int64_t F, int p
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        hu[i] = min((unit0 + lane + kWave * i) * 4 / D, G - 1);
+        hu[i] = min((unit0 + lane + kWave * i) * 4 / D, NC - 1);
     }
     if (lane < kMaxGroup) {
         L.M[lane] = -INFINITY;
@@ -499,10 +537,10 @@ __device__ void merge_body(const DecodeArgs& a, int s, int kvh, int64_t F, int p
     }
     __builtin_amdgcn_wave_barrier();
 
-    // Index of part k's first log-sum-exp (part_index(worker, slot, G, 0)).
+    // Index of part k's first log-sum-exp (part_index(worker, slot, NC, 0)).
     auto part_loc = [&](int k) -> int64_t {
         const int64_t wk = unit_runs ? owner_of(F + k, U, W) : wa + k;
-        return (int64_t)part_index(wk, k == 0 ? first_slot : 0, G, 0);
+        return (int64_t)part_index(wk, k == 0 ? first_slot : 0, NC, 0);
     };
     // Every slot of v is defined and read on every path (unused slots are zero
     // and weigh 0), so no load of the merge can be left pending where the
@@ -542,9 +580,9 @@ __device__ void merge_body(const DecodeArgs& a, int s, int kvh, int64_t F, int p
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h) {
             const float x = coherent_load1(lse_r, lse_off + 4 * h);
-            l[h] = (has && h < G) ? x : -INFINITY;
+            l[h] = (has && h < NC) ? x : -INFINITY;
         }
-        for (int h = 0; h < G; ++h) {
+        for (int h = 0; h < NC; ++h) {
             float lh = l[0];
 #pragma unroll
             for (int i = 1; i < kMaxGroup; ++i)
@@ -582,48 +620,58 @@ __device__ void merge_body(const DecodeArgs& a, int s, int kvh, int64_t F, int p
 #pragma unroll
     for (int i = 0; i < UPL; ++i) {
         const int u = unit0 + lane + kWave * i;
-        if (u < NU) {
-            const int h = u * 4 / D, d = u * 4 % D;
-            uint8_t* dst = a.out + (((size_t)s * a.num_q_heads + kvh * G + h) * D + d) * E;
+        const int h = u * 4 / D, d = u * 4 % D;
+        if (u < NU && h < active) {
+            uint8_t* dst = a.out + (col_offset<MQ>(a, s, kvh, row0, h, D) + d) * E;
             store4<DT>(dst, acc[i] * (1.f / L.den[h]));
         }
     }
     __builtin_amdgcn_wave_barrier();
 }
 
-template <int DT, int D>
-__device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int64_t F, int64_t Fv, int nb, int64_t U, int64_t W,
-                            MergeLds& L) {
+template <int DT, int D, bool MQ>
+__device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int64_t Fv, int nb,
+                            int64_t U, int64_t W, MergeLds& L) {
     const bool unit_runs = W >= U;
     const int64_t wa = owner_of(F, U, W);
     const int parts = unit_runs ? nb : (int)(owner_of(F + nb - 1, U, W) - wa + 1);
     // The owner of the first block used slot 0 if this pair was its first run,
     // i.e. its units begin at or after the pair's first unit Fv.
     const int first_slot = run_start(wa, U, W) >= Fv ? 0 : 1;
-    const int units = a.group * D / 4;  // 16-byte output units of the pair
+    const int units = a.cols * D / 4;  // 16-byte output units of the pair
     if (units <= kWave)
-        merge_body<DT, D, 1>(a, s, kvh, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+        merge_body<DT, D, 1, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
     else if (units <= 2 * kWave)
-        merge_body<DT, D, 2>(a, s, kvh, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+        merge_body<DT, D, 2, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
     else
         for (int u0 = 0; u0 < units; u0 += 4 * kWave)  // up to 256 units per pass
-            merge_body<DT, D, 4>(a, s, kvh, F, parts, wa, first_slot, unit_runs, U, W, u0, L);
+            merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, u0, L);
 }
 
 // Attend query group (s, kvh) over logical blocks [j0, j1) of sequence s, whose
 // pair (s, kvh) occupies units [F, F + nb).  A run over the whole context
 // writes out; otherwise the run stores a partial in slot `slot` of worker w,
-// and the wave that stores the pair's last partial merges them.
-template <int DT, int D, int B, bool APPEND>
-__device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0, int j1, int nb, int64_t F,
-                           int64_t Fv, int64_t U, int64_t W, int w, int slot, MergeLds& mlds) {
+// and the wave that stores the pair's last partial merges them.  With several
+// query tokens (MODE kModeMulti) the pair's columns are its `rows` query
+// tokens (from query row row0) times the G heads, and column (i, h) sees
+// positions up to ctx - rows + i; otherwise the columns are the G heads of
+// sequence s's one token, which sees positions up to ctx - 1.
+template <int DT, int D, int B, int MODE>
+__device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row0, int rows, int j0, int j1, int nb,
+                           int64_t F, int64_t Fv, int64_t U, int64_t W, int w, int slot, MergeLds& mlds) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
     constexpr int NBUF = PA_TILE_BUFFERS;
+    constexpr bool APPEND = MODE == kModeAppend, MQ = MODE == kModeMulti;
     const int lane = threadIdx.x & 63;
-    const int n = lane & 15;  // this lane's head column (and row within a 16-row piece)
+    const int n = lane & 15;  // this lane's column (and row within a 16-row piece)
     const int r = lane >> 4;  // this lane's group of 4 rows / k-range
     const int G = a.group;
+    const int active = MQ ? rows * G : G;  // columns that hold a query
+    const int qc = n < active ? n : 0;     // the column whose query this lane uses
+    // Last position this lane's column sees; a tile reaching past lim0 needs masking.
+    const int lim0 = MQ ? ctx - rows : ctx - 1;
+    const int lim = MQ ? lim0 + qc / G : lim0;
 
     // Block ids are read with scalar loads (the row of the table is the same for
     // the whole wave), one block ahead, so waiting for one never waits on the
@@ -631,14 +679,13 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     const ScalarPtr bt = (ScalarPtr)(a.block_tables + (size_t)s * a.max_blocks);
     int next_id = bt[j0];
 
-    // Q of the lane's head, in the B-operand form of the QK product.  Columns
-    // n >= G are padding: they take head 0's row, so they only repeat that
-    // head's scores (and its rescale decisions) and are never stored.  Every
-    // lane loads, so the load is not under a lane mask.
+    // Q of the lane's column, in the B-operand form of the QK product.  Columns
+    // n >= active are padding: they take column 0's row, so they only repeat
+    // its scores (and its rescale decisions) and are never stored.  Every lane
+    // loads, so the load is not under a lane mask.
     uint4 qf[C::kKFrag];
     {
-        const int hq = kvh * G + (n < G ? n : 0);
-        const uint8_t* qrow = a.q + ((size_t)s * a.num_q_heads + hq) * (size_t)(D * E);
+        const uint8_t* qrow = a.q + col_offset<MQ>(a, s, kvh, row0, qc, D) * E;
 #pragma unroll
         for (int f = 0; f < C::kKFrag; ++f) qf[f] = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * r);
     }
@@ -713,7 +760,7 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     auto consume = [&](int tau, Tile<DT, D, B>& t, bool may_be_partial) {
         const int j = j0 + tau / C::kSub, u = tau % C::kSub;
         const int tok0 = j * B + 16 * u + 4 * r;  // position of this lane's first row
-        const bool partial = may_be_partial && j * B + 16 * u + 16 > ctx;
+        const bool partial = may_be_partial && j * B + 16 * u + 16 > lim0 + 1;
         if constexpr (APPEND) {
             if (may_be_partial && owns_new && tau == tl_tile) {  // the tile holding the new token
                 if (n == tt) {
@@ -735,7 +782,7 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             z[e] = sc[e] * a.scale_log2;
-            if (partial && tok0 + e >= ctx) z[e] = -INFINITY;
+            if (partial && tok0 + e > lim) z[e] = -INFINITY;
         }
         const float tmax = row_group_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
         if (__builtin_amdgcn_read_exec() & __ballot(tmax > m + kLazy)) {
@@ -765,10 +812,12 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     // tile per step on every path, so the wait before consuming a tile counts
     // only the loads issued after it and never drains the ring; the first and
     // last steps are peeled.
-    // Only the last kSub tiles of a sequence can reach past its end; the
-    // steady loop stops early enough that those always fall in the peeled
-    // tail, so it never pays for masking.
-    constexpr int kTail = (NBUF - 1 > C::kSub ? NBUF - 1 : C::kSub);
+    // Only the last kSub tiles of a sequence can reach past its end (with
+    // several query tokens, up to 15 more positions are masked for some
+    // columns: one tile more); the steady loop stops early enough that those
+    // always fall in the peeled tail, so it never pays for masking.
+    constexpr int kMasked = MQ ? C::kSub + 1 : C::kSub;
+    constexpr int kTail = (NBUF - 1 > kMasked ? NBUF - 1 : kMasked);
     Tile<DT, D, B> buf[NBUF];
     if (ntiles < NBUF) {
 #pragma unroll
@@ -805,17 +854,19 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
 
     // Full denominator of the lane's head: the four row groups hold disjoint tokens.
     lsum = row_group_sum(lsum);
-    const float inv = 1.f / lsum;
+    // (A column that sees no position can only come from lengths that break
+    // the preconditions; it then gets 0 rather than 0/0.)
+    const float inv = MQ ? (lsum > 0.f ? 1.f / lsum : 0.f) : 1.f / lsum;
     if (j0 == 0 && j1 == nb) {
-        if (n < G) {
-            uint8_t* orow = a.out + ((size_t)s * a.num_q_heads + kvh * G + n) * (size_t)(D * E);
+        if (n < active) {
+            uint8_t* orow = a.out + col_offset<MQ>(a, s, kvh, row0, n, D) * E;
 #pragma unroll
             for (int c = 0; c < C::kVChunk; ++c) store4<DT>(orow + (16 * c + 4 * r) * E, O[c] * inv);
         }
         return;
     }
-    if (n < G) {
-        const size_t part = part_index(w, slot, G, n);
+    if (n < a.cols) {
+        const size_t part = part_index(w, slot, a.cols, n);
         float* po = a.part_o + part * D;
 #pragma unroll
         for (int c = 0; c < C::kVChunk; ++c)
@@ -829,7 +880,7 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int j0,
     const int parts = W >= U ? nb : (int)(owner_of(F + nb - 1, U, W) - owner_of(F, U, W) + 1);
     int last = 0;
     if (lane == 0) last = arrive(a.arrivals + (size_t)s * a.num_kv_heads + kvh, a.tag, parts) ? 1 : 0;
-    if (__shfl(last, 0)) merge_parts<DT, D>(a, s, kvh, F, Fv, nb, U, W, mlds);
+    if (__shfl(last, 0)) merge_parts<DT, D, MQ>(a, s, kvh, row0, active, F, Fv, nb, U, W, mlds);
 }
 
 // Fused append, the store side: wave `wi` of the writer workgroups copies the
@@ -914,10 +965,12 @@ constexpr size_t kDecodeStaticLds = sizeof(MergeLds) * kWavesPerGroup + sizeof(i
 #define PA_MIN_WAVES_PER_SIMD 1
 #endif
 
-template <int DT, int D, int B, bool APPEND>
+template <int DT, int D, int B, int MODE>
 __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
     using C = Cfg<DT, D, B>;
-    extern __shared__ int32_t s_lds[];  // ctx[num_seqs], pre[num_seqs + 1]
+    constexpr bool APPEND = MODE == kModeAppend, MQ = MODE == kModeMulti;
+    // ctx[num_seqs], pre[num_seqs + 1]; several query tokens: row0[num_seqs], rows[num_seqs]
+    extern __shared__ int32_t s_lds[];
     __shared__ int32_t s_wave_tot[kWavesPerGroup];
     __shared__ MergeLds s_merge[kWavesPerGroup];
     if constexpr (APPEND) {
@@ -928,7 +981,9 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
     }
     int32_t* s_ctx = s_lds;
     int32_t* s_pre = s_lds + a.num_seqs;
-    load_lengths<B>(a, s_ctx, s_pre, s_wave_tot);
+    int32_t* s_row0 = s_pre + a.num_seqs + 1;
+    int32_t* s_rows = s_row0 + a.num_seqs;
+    load_lengths<B, MQ>(a, s_ctx, s_pre, s_row0, s_rows, s_wave_tot);
 
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
@@ -936,13 +991,16 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
     const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
     const int W = a.num_workers;
 
-    // Sequences with no context get out = 0; worker w takes the pairs z = w (mod W).
+    // Query rows with no context get out = 0; worker w takes the pairs z = w (mod W).
     for (int z = w; z < S * Hkv; z += W) {
         const int s = z / Hkv, kvh = z % Hkv;
         if (s_ctx[s] != 0) continue;
-        uint8_t* orow = a.out + ((size_t)s * a.num_q_heads + (size_t)kvh * G) * (size_t)(D * C::kElt);
-        for (int i = lane; i < G * D * C::kElt / 16; i += kWave)
-            reinterpret_cast<uint4*>(orow)[i] = make_uint4(0, 0, 0, 0);
+        const int nrows = MQ ? s_rows[s] : 1;
+        for (int i = 0; i < nrows; ++i) {
+            uint8_t* orow = a.out + col_offset<MQ>(a, s, kvh, MQ ? s_row0[s] : 0, i * G, D) * C::kElt;
+            for (int k = lane; k < G * D * C::kElt / 16; k += kWave)
+                reinterpret_cast<uint4*>(orow)[k] = make_uint4(0, 0, 0, 0);
+        }
     }
 
     const int64_t U = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[S]) * Hkv;  // uniform: a scalar loop
@@ -971,9 +1029,11 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         const int jv1 = left < (int64_t)(nbv - jv0) ? jv0 + (int)left : nbv;
         const int j0 = jv0 > cost ? jv0 - cost : 0, j1 = jv1 - cost;
         const int64_t Fv = (int64_t)base * Hkv + (int64_t)kvh * nbv;  // the pair's first unit
+        const int row0 = MQ ? __builtin_amdgcn_readfirstlane(s_row0[s]) : 0;
+        const int rows = MQ ? __builtin_amdgcn_readfirstlane(s_rows[s]) : 1;
         if (j1 > j0)  // a range that ends inside the leading units holds no block
-            attend_run<DT, D, B, APPEND>(a, s, kvh, ctx, j0, j1, nb, Fv + cost, Fv, U, W, w, u == start ? 0 : 1,
-                                         s_merge[threadIdx.x >> 6]);
+            attend_run<DT, D, B, MODE>(a, s, kvh, ctx, row0, rows, j0, j1, nb, Fv + cost, Fv, U, W, w,
+                                       u == start ? 0 : 1, s_merge[threadIdx.x >> 6]);
         u += jv1 - jv0;
     }
 }
@@ -1103,10 +1163,11 @@ pa_status_t check_decode_shapes(int32_t num_seqs, int32_t num_q_heads, int32_t m
 }
 
 // Worker count and workspace layout; needs the device only for the automatic choice.
-// Workspace: arrival words [S * Hkv] (8 B each), then part_lse [W][2][G], then part_o [W][2][G][D].
+// Workspace: arrival words [S * Hkv] (8 B each), then part_lse [W][2][cols], then
+// part_o [W][2][cols][D], where cols is a pair's column count (G, or tokens x G).
 pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, const pa_cache_desc_t* cache,
-                      int32_t num_workers, Plan* plan) {
-    const int Hkv = cache->num_kv_heads, G = num_q_heads / Hkv, D = cache->head_dim;
+                      int32_t num_workers, int cols, Plan* plan) {
+    const int Hkv = cache->num_kv_heads, G = cols, D = cache->head_dim;
     *plan = Plan{0, 0, 0, 0, 0};
     if (num_workers == -1) {
         plan->workers = num_seqs * Hkv;
@@ -1144,9 +1205,15 @@ uint32_t next_tag() {
     return t;
 }
 
-template <int DT, int D, int B, bool APPEND>
+// LDS bytes of one decode workgroup's per-sequence arrays (the dynamic part).
+size_t decode_dynamic_lds(int num_seqs, bool multi) {
+    return sizeof(int32_t) * (2 * (size_t)num_seqs + 1 + (multi ? 2 * (size_t)num_seqs : 0));
+}
+
+template <int DT, int D, int B, int MODE>
 hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stream) {
     using C = Cfg<DT, D, B>;
+    constexpr bool APPEND = MODE == kModeAppend;
     const int groups = (plan.workers + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups == 0) return hipSuccess;
     DecodeArgs args_copy = a;
@@ -1158,39 +1225,65 @@ hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stre
         writer_groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
     }
     void* args[] = {&args_copy};
-    const size_t lds = sizeof(int32_t) * (2 * (size_t)a.num_seqs + 1);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, B, APPEND>),
+    const size_t lds = decode_dynamic_lds(a.num_seqs, MODE == kModeMulti);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, B, MODE>),
                            dim3(groups + writer_groups), dim3(kGroupThreads), args, lds, stream);
 }
 
-template <int DT, bool APPEND>
+template <int DT, int MODE>
 hipError_t dispatch_decode(const DecodeArgs& a, const Plan& plan, int D, int B, hipStream_t stream) {
     if (D == 64)
-        return B == 16 ? launch_decode<DT, 64, 16, APPEND>(a, plan, stream)
-                       : launch_decode<DT, 64, 32, APPEND>(a, plan, stream);
-    return B == 16 ? launch_decode<DT, 128, 16, APPEND>(a, plan, stream)
-                   : launch_decode<DT, 128, 32, APPEND>(a, plan, stream);
+        return B == 16 ? launch_decode<DT, 64, 16, MODE>(a, plan, stream)
+                       : launch_decode<DT, 64, 32, MODE>(a, plan, stream);
+    return B == 16 ? launch_decode<DT, 128, 16, MODE>(a, plan, stream)
+                   : launch_decode<DT, 128, 32, MODE>(a, plan, stream);
 }
 
-// Shared by pa_decode_ex and pa_decode_append (k_new/v_new non-null: fused append).
+template <int MODE>
+hipError_t dispatch_dtype(const DecodeArgs& a, const Plan& plan, const pa_cache_desc_t* cache, hipStream_t stream) {
+    const int D = cache->head_dim, B = cache->block_size;
+    switch (cache->dtype) {
+        case PA_F32:
+            return dispatch_decode<PA_F32, MODE>(a, plan, D, B, stream);
+        case PA_F16:
+            return dispatch_decode<PA_F16, MODE>(a, plan, D, B, stream);
+        default:
+            return dispatch_decode<PA_BF16, MODE>(a, plan, D, B, stream);
+    }
+}
+
+// Query tokens per pair when a sequence has several: as many as fit 16 columns.
+int tokens_per_pair(int num_q_heads, const pa_cache_desc_t* cache) {
+    const int G = num_q_heads / cache->num_kv_heads;
+    return G >= 16 ? 1 : 16 / G;
+}
+
+// Shared by pa_decode_ex, pa_decode_append (mode kModeAppend: k_new/v_new) and
+// pa_attend (mode kModeMulti: query_start and max_query_len).
 pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                        const int32_t* block_tables, const int32_t* context_lens, float scale, void* out,
-                        int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
-                        const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes, int32_t num_workers,
-                        bool append, pa_stream_t stream) {
+                        const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                        int32_t max_query_len, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                        int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
+                        size_t workspace_bytes, int32_t num_workers, int mode, pa_stream_t stream) {
     pa_status_t st = check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache);
     if (st != PA_OK) return st;
+    const bool append = mode == kModeAppend, multi = mode == kModeMulti;
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
-    if (num_seqs == 0) return PA_OK;  // nothing is touched, so empty tensors may pass null pointers
+    if (multi && max_query_len < 0) return PA_ERR_INVALID_ARG;
+    // nothing is touched, so empty tensors may pass null pointers
+    if (num_seqs == 0 || (multi && max_query_len == 0)) return PA_OK;
     if (!q || !k_cache || !v_cache || !context_lens || !out) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(context_lens, 4) || (block_tables && !aligned(block_tables, 4)))
         return PA_ERR_INVALID_ARG;
     if (append && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return PA_ERR_INVALID_ARG;
+    if (multi && (!query_start || !aligned(query_start, 4))) return PA_ERR_INVALID_ARG;
+    const int G = num_q_heads / cache->num_kv_heads;
+    const int tpc = multi ? tokens_per_pair(num_q_heads, cache) : 1;
     Plan plan;
-    st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, &plan);
+    st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, tpc * G, &plan);
     if (st != PA_OK) return st;
     if (plan.bytes > 0 && (workspace == nullptr || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
         return PA_ERR_WORKSPACE;
@@ -1220,6 +1313,9 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     a.num_blocks = cache->num_blocks;
     a.num_workers = plan.workers;
     a.per_segment = plan.per_segment;
+    a.cols = tpc * G;
+    a.query_start = query_start;
+    a.tpc = tpc;
     // A run start costs about as much as streaming kRunCostBytes of K/V: count
     // it as that many units so that workers with many short runs get fewer blocks.
     const size_t unit_bytes = (size_t)cache->block_size * cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2) * 2;
@@ -1229,24 +1325,24 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     int lds_max = 0;
     st = lds_limit(&lds_max);
     if (st != PA_OK) return st;
-    if (sizeof(int32_t) * (2 * (size_t)num_seqs + 1) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
+    if (decode_dynamic_lds(num_seqs, multi) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
 
     hipStream_t sm = static_cast<hipStream_t>(stream);
-    const int D = cache->head_dim, B = cache->block_size;
-    hipError_t e;
-    switch (cache->dtype) {
-        case PA_F32:
-            e = append ? dispatch_decode<PA_F32, true>(a, plan, D, B, sm) : dispatch_decode<PA_F32, false>(a, plan, D, B, sm);
-            break;
-        case PA_F16:
-            e = append ? dispatch_decode<PA_F16, true>(a, plan, D, B, sm) : dispatch_decode<PA_F16, false>(a, plan, D, B, sm);
-            break;
-        default:
-            e = append ? dispatch_decode<PA_BF16, true>(a, plan, D, B, sm)
-                       : dispatch_decode<PA_BF16, false>(a, plan, D, B, sm);
-            break;
+    if (!multi) {
+        const hipError_t e = append ? dispatch_dtype<kModeAppend>(a, plan, cache, sm)
+                                    : dispatch_dtype<kModeDecode>(a, plan, cache, sm);
+        return e == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
-    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+    // Several query tokens: launch c takes tokens [c * tpc, (c + 1) * tpc) of every
+    // sequence, so each launch's pairs fit one 16-column tile; the launches share
+    // the workspace in stream order.
+    const int chunks = (max_query_len + tpc - 1) / tpc;
+    for (int c = 0; c < chunks; ++c) {
+        a.chunk = c;
+        a.tag = next_tag();
+        if (dispatch_dtype<kModeMulti>(a, plan, cache, sm) != hipSuccess) return PA_ERR_HIP;
+    }
+    return PA_OK;
 }
 
 }  // namespace
@@ -1302,7 +1398,17 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32
                                     const pa_cache_desc_t* cache, int32_t num_workers) {
     if (check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache) != PA_OK) return 0;
     Plan plan;
-    if (make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, &plan) != PA_OK) return 0;
+    const int G = num_q_heads / cache->num_kv_heads;
+    if (make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, G, &plan) != PA_OK) return 0;
+    return plan.bytes;
+}
+
+size_t pa_attend_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                 const pa_cache_desc_t* cache, int32_t num_workers) {
+    if (check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache) != PA_OK) return 0;
+    Plan plan;
+    const int cols = tokens_per_pair(num_q_heads, cache) * (num_q_heads / cache->num_kv_heads);
+    if (make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, cols, &plan) != PA_OK) return 0;
     return plan.bytes;
 }
 
@@ -1316,8 +1422,18 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
                          size_t workspace_bytes, int32_t num_workers, pa_stream_t stream) {
     return decode_impl(q, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_tables,
-                       context_lens, scale, out, num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace,
-                       workspace_bytes, num_workers, false, stream);
+                       context_lens, nullptr, 1, scale, out, num_seqs, num_q_heads, max_blocks_per_seq, cache,
+                       workspace, workspace_bytes, num_workers, kModeDecode, stream);
+}
+
+pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_query_len,
+                      const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes, int32_t num_workers,
+                      pa_stream_t stream) {
+    return decode_impl(q, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_tables,
+                       context_lens, query_start, max_query_len, scale, out, num_seqs, num_q_heads,
+                       max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers, kModeMulti, stream);
 }
 
 pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -1325,8 +1441,9 @@ pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new
                              int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                              const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
                              int32_t num_workers, pa_stream_t stream) {
-    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs,
-                       num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers, true, stream);
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, scale, out,
+                       num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers,
+                       kModeAppend, stream);
 }
 
 pa_status_t pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

@@ -117,6 +117,35 @@ def test_decode_append_rejects(kw, status):
     assert _append(_desc(), **kw) == status
 
 
+def _attend_call(desc, *, qs=A, maxq=4, **kw):
+    base = dict(q=A, kc=A, vc=A, bt=A, ctx=A, out=A, S=2, Hq=4, maxblk=3, ws=A, ws_bytes=1 << 30, workers=64,
+                scale=0.125)
+    base.update(kw)
+    b = base
+    return pa.lib().pa_attend(b["q"], b["kc"], b["vc"], b["bt"], b["ctx"], qs, b["scale"], b["out"], b["S"], b["Hq"],
+                              b["maxblk"], maxq, ctypes.byref(desc), b["ws"], b["ws_bytes"], b["workers"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qs=None), INVALID), (dict(qs=A + 2), INVALID), (dict(maxq=-1), INVALID), (dict(q=None), INVALID),
+    (dict(Hq=3), INVALID), (dict(Hq=34), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
+    (dict(maxq=0, qs=None, q=None, out=None), OK), (dict(S=0, qs=None), OK),
+])
+def test_attend_rejects(kw, status):
+    assert _attend_call(_desc(), **kw) == status
+
+
+def test_attend_workspace_sizes():
+    L = pa.lib()
+    d = _desc(head_dim=128, num_kv_heads=8)
+    W_, S, D, Hkv = 100, 64, 128, 8
+    r = lambda x: (x + 255) // 256 * 256
+    for Hq, cols in [(32, 16), (56, 14), (8, 16), (128, 16)]:  # G = 4, 7, 1, 16: floor(16/G) tokens x G heads
+        got = L.pa_attend_workspace_bytes(S, Hq, 256, ctypes.byref(d), W_)
+        assert got == r(8 * S * Hkv) + r(4 * W_ * 2 * cols) + 4 * W_ * 2 * cols * D
+    assert L.pa_attend_workspace_bytes(S, 32, 256, ctypes.byref(d), -1) == 0
+
+
 def test_decode_zero_sequences_is_a_noop():
     assert _decode(_desc(), S=0) == OK
 

@@ -1,0 +1,118 @@
+"""GPU parity of pa_attend (several query tokens per sequence, causal) against
+the oracle, through the C ABI.  Pools hold every position (prefill and new
+tokens), written by the library's pa_write_kv; the oracle builds its own."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_slot_amd as pa
+from paged_kv_decode_slot_amd import workloads as W
+from tests.gpu_helpers import TOL, GpuCase, dev_bits, log, max_abs_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gpu(case: W.Case) -> GpuCase:
+    g = GpuCase(case)
+    g.append()  # every position is in the cache before attend
+    return g
+
+
+def _attend(g: GpuCase, mc: W.MultiCase, workers=0):
+    qs = torch.from_numpy(mc.query_start).to(DEV)
+    return pa.attend(mc.q.to(DEV), g.k_cache, g.v_cache, g.bt, g.ctx, qs, mc.max_q_len, g.case.scale,
+                     num_workers=workers)
+
+
+def _oracle(mc: W.MultiCase) -> np.ndarray:
+    c = mc.base
+    kp, vp = oracle.build_pools(c)
+    return oracle.attend(mc.q, kp, vp, c.block_tables, c.context_lens, mc.query_start, c.scale,
+                         Hkv=c.Hkv, B=c.B)
+
+
+def _q_lens(case: W.Case, kind: str, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    ctx = case.context_lens.astype(np.int64)
+    if kind == "one":
+        return np.ones(case.S, dtype=np.int64)
+    if kind == "spec4":
+        return np.full(case.S, 4)
+    if kind == "full":  # the whole context is the prompt
+        return ctx.copy()
+    # a mix of decode tokens, short drafts and prompt chunks
+    return rng.choice([0, 1, 1, 2, 3, 5, 16, 17, 40], size=case.S)
+
+
+SHAPES = [
+    (dict(S=5, Hq=8, Hkv=2, D=128, B=16, dtype="bf16", ctx_range=(1, 300)), "mix"),
+    (dict(S=3, Hq=16, Hkv=1, D=64, B=32, dtype="f16", ctx_range=(1, 200)), "mix"),  # G = 16: one token a pair
+    (dict(S=7, Hq=3, Hkv=3, D=128, B=32, dtype="bf16", ctx_range=(1, 100)), "spec4"),  # G = 1: 16 tokens a pair
+    (dict(S=4, Hq=7, Hkv=1, D=128, B=16, dtype="f32", ctx_range=(1, 90)), "mix"),  # G = 7: 2 tokens, 14 columns
+    (dict(S=6, Hq=4, Hkv=2, D=64, B=32, dtype="f32", ctx_range=(1, 150)), "full"),
+    (dict(S=8, Hq=6, Hkv=2, D=128, B=32, dtype="bf16", ctx=[0, 1, 15, 16, 17, 32, 33, 0],
+          max_blocks_per_seq=4), "full"),
+    (dict(S=9, Hq=12, Hkv=4, D=64, B=16, dtype="f16", ctx_range=(1, 700)), "mix"),
+    (dict(S=1, Hq=4, Hkv=1, D=64, B=16, dtype="bf16", ctx=[3000]), "spec4"),
+]
+
+
+@pytest.mark.parametrize("workers", [0, -1, 3, 10000])
+@pytest.mark.parametrize("idx", range(len(SHAPES)))
+def test_attend_small_shapes(idx, workers):
+    kw, kind = SHAPES[idx]
+    case = W.make_case(seed=300 + idx, name=f"mq{idx}", **kw)
+    mc = W.with_queries(case, _q_lens(case, kind, 400 + idx), seed=500 + idx)
+    log(f"[attend] shape {idx} ({kind}) workers {workers} q_lens {mc.q_lens.tolist()[:10]}")
+    out = _attend(_gpu(case), mc, workers)
+    torch.cuda.synchronize()
+    assert max_abs_err(out, _oracle(mc)) <= TOL[case.dtype]
+
+
+@pytest.mark.parametrize("workers", [0, 37])
+def test_attend_one_token_each_is_decode_bitwise(workers):
+    case = W.config_case(3)
+    g = _gpu(case)
+    mc = W.MultiCase(base=case, q=case.q.clone(), query_start=np.arange(case.S + 1, dtype=np.int32))
+    log(f"[attend] one token each, C3, workers {workers}")
+    a = _attend(g, mc, workers)
+    d = g.decode(num_workers=workers)
+    torch.cuda.synchronize()
+    assert torch.equal(dev_bits(a), dev_bits(d))
+
+
+def test_attend_speculative_verify_llama3_shape():
+    # Four draft tokens per sequence on the Llama-3-8B-shaped batch: one launch,
+    # every K/V row read once.
+    case = W.config_case(3)
+    mc = W.with_queries(case, np.full(case.S, 4), seed=601)
+    log("[attend] C3 with 4 query tokens per sequence")
+    out = _attend(_gpu(case), mc)
+    torch.cuda.synchronize()
+    assert max_abs_err(out, _oracle(mc)) <= TOL[case.dtype]
+
+
+def test_attend_prompt_chunks_mixed_with_decode():
+    case = W.make_case(S=6, Hq=32, Hkv=8, D=128, B=16, dtype="bf16", ctx_range=(300, 2000), seed=611, name="mix")
+    mc = W.with_queries(case, [1, 1, 64, 300, 1, 17], seed=612)
+    log(f"[attend] chunked prompts with decode, q_lens {mc.q_lens.tolist()}")
+    g = _gpu(case)
+    out = _attend(g, mc)
+    again = _attend(g, mc)
+    torch.cuda.synchronize()
+    assert max_abs_err(out, _oracle(mc)) <= TOL[case.dtype]
+    assert torch.equal(dev_bits(out), dev_bits(again))  # run to run, bitwise
+
+
+def test_attend_no_query_tokens_is_a_noop():
+    case = W.make_case(S=3, Hq=4, Hkv=2, D=64, B=16, dtype="f16", ctx_range=(5, 40), seed=621, name="none")
+    g = _gpu(case)
+    qs = torch.zeros(case.S + 1, dtype=torch.int32, device=DEV)
+    q = torch.empty((0, case.Hq, case.D), dtype=torch.float16, device=DEV)
+    out = pa.attend(q, g.k_cache, g.v_cache, g.bt, g.ctx, qs, 0, case.scale)
+    torch.cuda.synchronize()
+    assert out.shape == (0, case.Hq, case.D)
