@@ -61,7 +61,7 @@ def setup_layers(case, layers, device, num_workers):
     if case.k_prefill.shape[0]:
         pa.write_kv(case.k_prefill.to(device), case.v_prefill.to(device),
                     torch.from_numpy(case.slot_prefill).to(device), k0, v0)
-    steps = []
+    steps, pools = [], []
     for i in range(layers):
         kc, vc = (k0, v0) if i == 0 else (k0.clone(), v0.clone())
         out = torch.empty_like(q)
@@ -69,8 +69,9 @@ def setup_layers(case, layers, device, num_workers):
                       pa.prepare_decode(q, kc, vc, bt, ctx, case.scale, out, num_workers=num_workers),
                       pa.prepare_decode_append(q, k_new, v_new, kc, vc, bt, ctx, case.scale, out,
                                                num_workers=num_workers)))
+        pools.append((kc, vc))
     torch.cuda.synchronize()
-    return steps
+    return steps, pools
 
 
 def _events(n):
@@ -129,7 +130,7 @@ def measure(n, args, device):
     log(f"[bench] workload {n}: inputs drawn in {time.perf_counter() - t:.1f}s")
     layer_bytes = 2 * case.pool_numel * case.elt
     layers = args.layers or max(2, math.ceil(2 * 2**30 / layer_bytes))
-    steps = setup_layers(case, layers, device, args.workers)
+    steps, _pools = setup_layers(case, layers, device, args.workers)
     K, Wm = args.steps, args.warmup
     log(f"[bench] workload {n}: {layers} layers of {layer_bytes / 1e9:.2f} GB; timing {K} steps")
     # The timed region: K fused steps back to back (the headline).
@@ -165,6 +166,36 @@ def measure(n, args, device):
                                 p90=pct(t_decode, 90)),
         t_write_us_events=dict(mean=statistics.fmean(t_write), p50=pct(t_write, 50)),
     )
+
+
+def measure_attend(n, q_len, args, device):
+    """pa_attend with q_len query tokens per sequence (e.g. draft tokens being
+    verified) over workload n's pools, K steps back to back."""
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+    from paged_kv_decode_slot_amd import workloads as W
+
+    case = W.config_case(n)
+    mc = W.with_queries(case, [q_len] * case.S, seed=1000 + n)
+    layer_bytes = 2 * case.pool_numel * case.elt
+    layers = args.layers or max(2, math.ceil(2 * 2**30 / layer_bytes))
+    steps, pools = setup_layers(case, layers, device, args.workers)
+    for (w, _d, _f) in steps:  # every position, the query tokens' own included, is in the cache
+        w()
+    q = mc.q.to(device)
+    qs = torch.from_numpy(mc.query_start).to(device)
+    bt = torch.from_numpy(case.block_tables).to(device)
+    ctx = torch.from_numpy(case.context_lens).to(device)
+    out = torch.empty_like(q)
+    calls = [pa.prepare_attend(q, kc, vc, bt, ctx, qs, mc.max_q_len, case.scale, out, num_workers=args.workers)
+             for (kc, vc) in pools]
+    ms = time_back_to_back(calls, args.steps, args.warmup)
+    us = ms * 1e3 / args.steps
+    b = W.attend_bytes(mc)
+    return dict(workload=W.CONFIGS[n]["name"], query_tokens_per_seq=q_len, us=round(us, 2),
+                bytes=b, gbs=round(b / (us * 1e-6) / 1e9, 1), frac_of_peak=round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                query_rows_per_s=round(int(mc.query_start[-1]) * case.Hq / (us * 1e-6)))
 
 
 # Measured HBM traffic of the decode kernel (two rocprofv3 counter passes, scaled by a
@@ -225,6 +256,8 @@ def main():
     ap.add_argument("--workers", type=int, default=0, help="decode work split (0 automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--attend-q", type=int, default=4,
+                    help="also time pa_attend with this many query tokens per sequence (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -270,6 +303,11 @@ def main():
             seq_heads_per_s=round(r["seq_heads_per_s"]), layers=r["layers"],
             step_bytes=r["step_bytes"], context_tokens=int(c.context_lens.sum()))
         del c, r
+        torch.cuda.empty_cache()
+
+    attend = None
+    if args.attend_q > 0:
+        attend = measure_attend(args.config, args.attend_q, args, device)
         torch.cuda.empty_cache()
 
     cpu = None
@@ -328,6 +366,7 @@ def main():
                 "t_write_us_per_launch_events": r2(main_res["t_write_us_events"]),
                 "t_decode_us_per_launch_events": r2(main_res["t_decode_us_events"]),
             },
+            "attend": attend,
             "other": other,
         },
     }
