@@ -496,6 +496,9 @@ constexpr int kCoherentPolicy = 16;
 __device__ inline f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_offset, 0, kCoherentPolicy));
 }
+__device__ inline void coherent_store4(__amdgpu_buffer_rsrc_t r, int byte_offset, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_offset, 0, kCoherentPolicy);
+}
 __device__ inline float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_offset) {
     return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_offset, 0, kCoherentPolicy));
 }
@@ -643,6 +646,10 @@ __device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int row0, int a
         merge_body<DT, D, 1, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
     else if (units <= 2 * kWave)
         merge_body<DT, D, 2, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+    else if (units <= 4 * kWave)
+        merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+    else if (MQ && units <= 8 * kWave)  // 16 columns of D = 128: one pass, 2 parts a batch
+        merge_body<DT, D, 8, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
     else
         for (int u0 = 0; u0 < units; u0 += 4 * kWave)  // up to 256 units per pass
             merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, u0, L);
@@ -865,14 +872,15 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row
         }
         return;
     }
-    if (n < a.cols) {
-        const size_t part = part_index(w, slot, a.cols, n);
-        float* po = a.part_o + part * D;
+    {
+        // The partial's outputs as 16-byte stores with the agent-coherence bit
+        // (through a resource bounded to this part, so lanes past a.cols store nothing).
+        const size_t part0 = part_index(w, slot, a.cols, 0);
+        const __amdgpu_buffer_rsrc_t po = __builtin_amdgcn_make_buffer_rsrc(a.part_o + part0 * D, (short)0,
+                                                                             a.cols * D * 4, kBufferWord3);
 #pragma unroll
-        for (int c = 0; c < C::kVChunk; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) coherent_store(po + 16 * c + 4 * r + e, O[c][e] * inv);
-        if (r == 0) coherent_store(a.part_lse + part, m + __log2f(lsum));
+        for (int c = 0; c < C::kVChunk; ++c) coherent_store4(po, (n * D + 16 * c + 4 * r) * 4, O[c] * inv);
+        if (n < a.cols && r == 0) coherent_store(a.part_lse + part0 + n, m + __log2f(lsum));
     }
     // Publish the partial (wait until its device-coherent stores are done),
     // then count it; the wave that stores the last part merges.
