@@ -48,6 +48,10 @@ def _load():
         lib.oracle_decode.restype = I
         lib.oracle_attend.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I, I, I, I, I, I, I, I]
         lib.oracle_attend.restype = I
+        lib.oracle_rope.argtypes = [P, P, P, I64, I, I, I, ctypes.c_double]
+        lib.oracle_rope.restype = I
+        lib.oracle_round.argtypes = [P, I64, I, P]
+        lib.oracle_round.restype = I
         lib.oracle_widen.argtypes = [P, I64, I, P]
         lib.oracle_widen.restype = None
         _lib = lib
@@ -136,6 +140,41 @@ def attend(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_ta
     if rc:
         raise ValueError("oracle_attend: bad argument")
     return out
+
+
+def rope(x: torch.Tensor, positions: np.ndarray, theta: float) -> np.ndarray:
+    """float64 rotary embedding of x [T, H, D] (storage dtype) at positions [T]."""
+    T, H, D = x.shape
+    pos = np.ascontiguousarray(positions, dtype=np.int32)
+    assert pos.shape == (T,)
+    out = np.empty((T, H, D), dtype=np.float64)
+    rc = _load().oracle_rope(_ptr(x.contiguous()), _ptr(pos), _ptr(out), T, H, D, _DTYPE_CODE[x.dtype], float(theta))
+    if rc:
+        raise ValueError("oracle_rope: bad argument")
+    return out
+
+
+def round_to(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
+    """x (float64) rounded once, to nearest with ties to even, into dtype."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    rc = _load().oracle_round(_ptr(x), x.size, _DTYPE_CODE[dtype], _ptr(out))
+    if rc:
+        raise ValueError("oracle_round: bad dtype")
+    return torch.from_numpy(out).to(dtype)  # exact: every value is representable
+
+
+def rope_case(case, theta: float):
+    """The decode step of ``case`` with RoPE applied: q and the new token's K rows
+    rotated at position ctx - 1 and rounded into the dtype; the prefill rows are
+    taken as already rotated.  Returns a copy of the case with those rows."""
+    import dataclasses
+
+    pos = np.maximum(case.context_lens.astype(np.int64) - 1, 0).astype(np.int32)
+    dt = case.q.dtype
+    q = round_to(rope(case.q, pos, theta), dt)
+    k_new = round_to(rope(case.k_new, pos, theta), dt)
+    return dataclasses.replace(case, q=q, k_new=k_new)
 
 
 def build_pools(case):

@@ -344,6 +344,80 @@ int oracle_attend(const void* q, const void* k_pool, const void* v_pool, const i
     return status;
 }
 
+/*
+ * Rotary position embedding, the rotate-half pairing of the Llama family
+ * (ForgeLLM README, feature list: RoPE in the Llama-family decoder; the
+ * paragraph after its quick start: RoPE scaling is not supported, so the
+ * plain form is the one to compute).  For a row x of D values at position p,
+ * with w_i = theta^(-2i/D) for i < D/2:
+ *   x'_i       = x_i cos(p w_i) - x_{i+D/2} sin(p w_i)
+ *   x'_{i+D/2} = x_{i+D/2} cos(p w_i) + x_i sin(p w_i)
+ * x: [T][H][D] in the storage dtype, pos: int32 [T]; out: double [T][H][D],
+ * the rotated values before any rounding.
+ */
+int oracle_rope(const void* x, const int32_t* pos, double* out, int64_t T, int H, int D, int dtype, double theta) {
+    if (D <= 0 || D % 2 || H <= 0 || theta <= 1.0) return -1;
+    int half = D / 2;
+    for (int64_t t = 0; t < T; ++t) {
+        double p = (double)pos[t];
+        for (int h = 0; h < H; ++h) {
+            size_t row = ((size_t)t * H + h) * (size_t)D;
+            for (int i = 0; i < half; ++i) {
+                double w = pow(theta, -2.0 * i / D);
+                double c = cos(p * w), sn = sin(p * w);
+                double a = widen(x, row + i, dtype), b = widen(x, row + i + half, dtype);
+                out[row + i] = a * c - b * sn;
+                out[row + i + half] = b * c + a * sn;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Round doubles to the nearest value of the storage dtype, ties to even, in
+ * one step (no intermediate float): out holds doubles that the dtype
+ * represents exactly.  For a type with m mantissa bits, minimum normal
+ * exponent emin and largest finite value vmax, |x| = q * 2^e with
+ * q in [2^m, 2^(m+1)) (or e = emin - m below the normal range) is rounded by
+ * rounding q to an integer.
+ */
+int oracle_round(const double* in, int64_t n, int dtype, double* out) {
+    int m, emin;
+    double vmax;
+    if (dtype == 0) {
+        for (int64_t k = 0; k < n; ++k) out[k] = (double)(float)in[k];
+        return 0;
+    } else if (dtype == 1) {
+        m = 10;
+        emin = -14;
+        vmax = 65504.0;
+    } else if (dtype == 2) {
+        m = 7;
+        emin = -126;
+        vmax = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    } else {
+        return -1;
+    }
+    for (int64_t k = 0; k < n; ++k) {
+        double x = in[k], ax = fabs(x);
+        if (isnan(x) || isinf(x) || ax == 0.0) {
+            out[k] = x;
+            continue;
+        }
+        int e2;
+        frexp(ax, &e2); /* ax = f * 2^e2, f in [0.5, 1) */
+        int e = e2 - 1 - m;
+        if (e2 - 1 < emin) e = emin - m;
+        double r = nearbyint(ldexp(ax, -e)) ; /* round half to even in the default mode */
+        double v = ldexp(r, e);
+        /* values at or above the midpoint between vmax and the next power step overflow */
+        if (v > vmax) v = INFINITY;
+        out[k] = x < 0 ? -v : v;
+    }
+    return 0;
+}
+
 /* Exposes the element widening on its own, so it can be checked against other converters. */
 void oracle_widen(const void* src, int64_t n, int dtype, double* dst) {
     for (int64_t i = 0; i < n; ++i) dst[i] = widen(src, (size_t)i, dtype);

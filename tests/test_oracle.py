@@ -439,3 +439,90 @@ def test_attend_thread_count_does_not_change_bits():
     c = _case(S=4, Hq=8, Hkv=2, D=64, B=16, dtype="f16", ctx_range=(5, 80), seed=91)
     mc = W.with_queries(c, [3, 5, 1, 4], seed=92)
     assert np.array_equal(_attend(mc, threads=1), _attend(mc, threads=7))
+
+
+# --- RoPE (rotate-half pairing) and the single rounding into the dtype ---
+
+def _rope_np(x, pos, theta):
+    """The same rotation as complex multiplication: (x_i + i x_{i+D/2}) * exp(i p w_i)."""
+    D = x.shape[-1]
+    w = theta ** (-2.0 * np.arange(D // 2) / D)
+    z = (x[..., :D // 2] + 1j * x[..., D // 2:]) * np.exp(1j * pos[:, None, None] * w[None, None, :])
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128), ("f16", 128)])
+def test_rope_matches_complex_rotation(dtype, D):
+    rng = np.random.default_rng(5)
+    x = W._normal(rng, (7, 3, D), dtype)
+    pos = np.array([0, 1, 2, 17, 1000, 4095, 131071], dtype=np.int32)
+    got = oracle.rope(x, pos, 10000.0)
+    ref = _rope_np(x.double().numpy(), pos.astype(np.float64), 10000.0)
+    assert np.max(np.abs(got - ref)) <= 1e-9 * np.max(np.abs(ref))
+
+
+def test_rope_position_zero_is_identity_and_pairs_keep_their_norm():
+    rng = np.random.default_rng(6)
+    x = W._normal(rng, (5, 2, 64), "f32")
+    pos = np.array([0, 3, 9, 100, 5000], dtype=np.int32)
+    got = oracle.rope(x, pos, 500000.0)
+    xd = x.double().numpy()
+    assert np.array_equal(got[0], xd[0])
+    n_in = xd[..., :32] ** 2 + xd[..., 32:] ** 2
+    n_out = got[..., :32] ** 2 + got[..., 32:] ** 2
+    assert np.max(np.abs(n_in - n_out)) <= 1e-12 * np.max(n_in)
+
+
+def test_rope_first_pair_turns_by_the_position_in_radians():
+    # w_0 = theta^0 = 1: dims 0 and D/2 rotate by exactly p radians.
+    x = torch.zeros((3, 1, 64), dtype=torch.float32)
+    x[:, 0, 0] = 1.0
+    pos = np.array([1, 2, 3], dtype=np.int32)
+    got = oracle.rope(x, pos, 10000.0)
+    for t, p in enumerate(pos):
+        assert got[t, 0, 0] == pytest.approx(np.cos(p), abs=1e-15)
+        assert got[t, 0, 32] == pytest.approx(np.sin(p), abs=1e-15)
+    # the last pair turns at w = theta^(-(D-2)/D)
+    x = torch.zeros((1, 1, 64), dtype=torch.float32)
+    x[0, 0, 31] = 1.0
+    got = oracle.rope(x, np.array([1000], dtype=np.int32), 10000.0)
+    w = 10000.0 ** (-62 / 64)
+    assert got[0, 0, 31] == pytest.approx(np.cos(1000 * w), abs=1e-13)
+    assert got[0, 0, 63] == pytest.approx(np.sin(1000 * w), abs=1e-13)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    rng = np.random.default_rng(7)
+    q = W._normal(rng, (1, 1, 128), "f32")
+    k = W._normal(rng, (1, 1, 128), "f32")
+    def score(m, n):
+        a = oracle.rope(q, np.array([m], dtype=np.int32), 10000.0)[0, 0]
+        b = oracle.rope(k, np.array([n], dtype=np.int32), 10000.0)[0, 0]
+        return float(a @ b)
+    for m, n in [(5, 2), (40, 37), (1003, 1000)]:
+        assert score(m, n) == pytest.approx(score(m - n, 0), rel=1e-10, abs=1e-10)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_round_matches_single_rounding_of_floats(dtype):
+    # For values a float holds exactly, one rounding from double must equal
+    # torch's float -> dtype rounding (itself to nearest, ties to even).
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(200000) * rng.choice([1e-6, 1e-3, 1.0, 30.0, 3e4], 200000)).astype(np.float32)
+    # add exact ties: midpoints between neighbouring dtype values
+    a = torch.from_numpy(x[:1000]).to(dtype)
+    b = torch.nextafter(a.float(), torch.full_like(a.float(), float("inf"))).to(dtype)
+    mids = ((a.double() + b.double()) / 2).float().numpy()
+    x = np.concatenate([x, mids])
+    got = oracle.round_to(x.astype(np.float64), dtype)
+    ref = torch.from_numpy(x).to(dtype)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+def test_round_is_one_step_from_double():
+    # 1 + 2^-8 + 2^-30 lies just above the bf16 midpoint 1 + 2^-8: one rounding
+    # gives 1 + 2^-7; rounding to float first would land on the midpoint and
+    # then round to even, 1.
+    x = np.array([1.0 + 2.0 ** -8 + 2.0 ** -30, -(1.0 + 2.0 ** -8 + 2.0 ** -30)])
+    got = oracle.round_to(x, torch.bfloat16).double().numpy()
+    assert list(got) == [1.0 + 2.0 ** -7, -(1.0 + 2.0 ** -7)]
