@@ -168,6 +168,38 @@ pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new
                              int32_t num_workers, pa_stream_t stream);
 
 /*
+ * Rotary position embedding in place, the rotate-half pairing of the Llama
+ * family (ForgeLLM README, feature list: RoPE in the Llama-family decoder;
+ * the paragraph after its quick start: RoPE scaling is not supported, so this
+ * is the plain form).  For every token t and head, with p = positions[t] and
+ * w_i = rope_theta^(-2i/D), i < D/2, dims i and i + D/2 of the row become
+ *   x_i cos(p w_i) - x_{i+D/2} sin(p w_i),   x_{i+D/2} cos(p w_i) + x_i sin(p w_i)
+ * rounded to nearest-even into the dtype.  The angle is formed and reduced in
+ * double; sin, cos and the rotation are single precision.
+ *   q : [num_tokens][num_q_heads][head_dim], k : [num_tokens][num_kv_heads][head_dim],
+ *       16-byte aligned, rotated in place (NULL allowed when its head count is 0)
+ *   positions : int32 [num_tokens], device
+ *   rope_theta : finite, > 1;  head_dim 64 or 128;  dtype a pa_dtype_t
+ */
+pa_status_t pa_rope(void* q, void* k, const int32_t* positions, int32_t num_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype, float rope_theta, pa_stream_t stream);
+
+/*
+ * One decoder step's attention in one launch, rotary embedding included:
+ * bitwise the same output and caches as
+ *    pa_rope(q', k_new', positions = context_lens - 1, ...)   on copies q', k_new'
+ *    pa_decode_append(q', k_new', v_new, ...)
+ * with the same num_workers; q and k_new are only read.  16-bit caches only
+ * (PA_ERR_UNSUPPORTED for f32: call the pair above).  Arguments as in
+ * pa_decode_append, plus rope_theta as in pa_rope.
+ */
+pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                  float rope_theta, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
+                                  size_t workspace_bytes, int32_t num_workers, pa_stream_t stream);
+
+/*
  * Attention of several query tokens per sequence over the paged cache: the
  * causal extension of pa_decode, for prompts split into chunks that run
  * alongside decode steps and for checking speculative draft tokens (ForgeLLM

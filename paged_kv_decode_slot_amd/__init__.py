@@ -13,13 +13,16 @@ from .binding import (  # noqa: F401
     cache_shapes,
     decode,
     decode_append,
+    decode_rope_append,
     lib,
     library_path,
     new_cache,
     prepare_attend,
     prepare_decode,
     prepare_decode_append,
+    prepare_decode_rope_append,
     prepare_write_kv,
+    rope,
     workspace_bytes,
     write_kv,
 )

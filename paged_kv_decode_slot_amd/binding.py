@@ -27,6 +27,8 @@ EXPORTS = (
     "pa_decode_append",
     "pa_attend",
     "pa_attend_workspace_bytes",
+    "pa_rope",
+    "pa_decode_rope_append",
     "pa_decode_workspace_bytes",
     "pa_decode_workspace_bytes_ex",
     "pa_status_string",
@@ -73,6 +75,11 @@ def lib() -> ctypes.CDLL:
         L.pa_attend.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, I32, DP, P, SZ, I32, P]
         L.pa_attend.restype = ctypes.c_int
         L.pa_attend_workspace_bytes.argtypes = [I32, I32, I32, DP, I32]
+        L.pa_rope.argtypes = [P, P, P, I32, I32, I32, I32, I32, ctypes.c_float, P]
+        L.pa_rope.restype = ctypes.c_int
+        L.pa_decode_rope_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, ctypes.c_float, P, I32, I32, I32,
+                                            DP, P, SZ, I32, P]
+        L.pa_decode_rope_append.restype = ctypes.c_int
         L.pa_attend_workspace_bytes.restype = SZ
         L.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, DP]
         L.pa_decode_workspace_bytes.restype = SZ
@@ -348,6 +355,55 @@ def prepare_attend(q, k_cache, v_cache, block_tables, context_lens, query_start,
 
     def call():
         _check("pa_attend", fn(*args))
+        return keep[5]
+
+    return call
+
+
+def rope(q: torch.Tensor, k: torch.Tensor, positions: torch.Tensor, rope_theta: float) -> None:
+    """Rotary embedding in place: q [T, Hq, D] and k [T, Hkv, D] at positions (int32 [T])."""
+    dev = _dev(q, k, positions)
+    if q.dim() != 3 or k.dim() != 3 or q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2] \
+            or q.dtype != k.dtype or not (q.is_contiguous() and k.is_contiguous()):
+        raise ValueError("q and k must be contiguous [T, H, D] of one dtype")
+    if positions.dtype != torch.int32 or positions.shape != (q.shape[0],) or not positions.is_contiguous():
+        raise ValueError("positions must be contiguous int32 [T]")
+    T, Hq, D = q.shape
+    with torch.cuda.device(dev):
+        st = lib().pa_rope(q.data_ptr(), k.data_ptr(), positions.data_ptr(), T, Hq, k.shape[1], D,
+                           _DTYPE_CODE[q.dtype], ctypes.c_float(rope_theta), _stream(dev))
+    _check("pa_rope", st)
+
+
+def _rope_append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, rope_theta, out,
+                      num_workers, workspace):
+    dev, out, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                                        out, num_workers, workspace)
+    # pa_decode_append arguments: (q, kn, vn, k, v, bt, ctx, scale, out, S, Hq, maxblk, desc, ws, ws_n, wk, st)
+    args = args[:8] + (ctypes.c_float(rope_theta),) + args[8:]
+    return dev, out, args, keep
+
+
+def decode_rope_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, rope_theta,
+                       out=None, *, num_workers=0, workspace=None):
+    """decode_append with the rotary embedding of q and k_new (at position ctx - 1) in the same launch."""
+    dev, out, args, _keep = _rope_append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                              scale, rope_theta, out, num_workers, workspace)
+    with torch.cuda.device(dev):
+        st = lib().pa_decode_rope_append(*args)
+    _check("pa_decode_rope_append", st)
+    return out
+
+
+def prepare_decode_rope_append(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, rope_theta,
+                               out=None, *, num_workers=0, workspace=None):
+    """Validate once; return a no-argument callable issuing the same pa_decode_rope_append."""
+    _dev_, out, args, keep = _rope_append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                               scale, rope_theta, out, num_workers, workspace)
+    fn = lib().pa_decode_rope_append
+
+    def call():
+        _check("pa_decode_rope_append", fn(*args))
         return keep[5]
 
     return call

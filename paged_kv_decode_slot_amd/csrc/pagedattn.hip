@@ -56,6 +56,7 @@ constexpr int kMaxGroup = 16;
 constexpr int kWorkersPerCU = PA_WORKERS_PER_CU;
 constexpr int kMinBlocksPerWorker = 16;
 constexpr int kMaxWorkers = 1 << 20;
+constexpr int kMaxRopePairs = 64;  // head_dim / 2
 #ifndef PA_RUN_COST_BYTES
 #define PA_RUN_COST_BYTES 49152
 #endif
@@ -233,6 +234,8 @@ struct DecodeArgs {
     const int32_t* query_start;  // several query tokens: [num_seqs + 1] query rows of each sequence
     int32_t chunk;        // several query tokens: this launch takes tokens [chunk*tpc, (chunk+1)*tpc) of each
     int32_t tpc;          // several query tokens: tokens per pair (16 / G)
+    int32_t rope;         // append: 1 = rotate q and the new K rows at position ctx - 1 first
+    double rope_w[kMaxRopePairs];  // rotary frequencies theta^(-2i/D), i < D/2
 };
 
 // What a decode_kernel instantiation computes: one query token per sequence,
@@ -418,6 +421,112 @@ __device__ inline void put_v_row(uint4& v, int e, const uint32_t* vals) {
         if (e == 1) v.y = vals[0];
         if (e == 2) v.z = vals[0];
         if (e == 3) v.w = vals[0];
+    }
+}
+
+// ---------------------------------------------------------------- rotary embedding
+
+// Rotary embedding, rotate-half pairing: dims i and i + D/2 turn by pos * w_i.
+// Everything runs in double with every operation spelled out (no
+// contraction, no library call whose code could differ between call sites),
+// and the result is rounded once to float, so every kernel that rotates
+// produces the same bits: the angle (up to 10^5 radians for the first pairs
+// at long contexts) is reduced by multiples of pi/2, and sin and cos of the
+// remainder r in [-pi/4, pi/4] come from their Taylor series to the r^17 and
+// r^16 terms (Horner form), whose remainder there is below 1e-18.
+__device__ inline void rope_cs(double w, int pos, double& c, double& s) {
+#pragma clang fp contract(off)
+    constexpr double kHalfPi = 1.5707963267948966;
+    const double ang = (double)pos * w;
+    const double k = rint(ang * (1.0 / kHalfPi));
+    const double r = fma(-kHalfPi, k, ang);
+    const double r2 = r * r;
+    double ps = -1.0 / 1307674368000.0 + r2 * (1.0 / 355687428096000.0);
+    ps = 1.0 / 6227020800.0 + r2 * ps;
+    ps = -1.0 / 39916800.0 + r2 * ps;
+    ps = 1.0 / 362880.0 + r2 * ps;
+    ps = -1.0 / 5040.0 + r2 * ps;
+    ps = 1.0 / 120.0 + r2 * ps;
+    ps = -1.0 / 6.0 + r2 * ps;
+    const double sr = r + (r * r2) * ps;
+    double pc = -1.0 / 87178291200.0 + r2 * (1.0 / 20922789888000.0);
+    pc = 1.0 / 479001600.0 + r2 * pc;
+    pc = -1.0 / 3628800.0 + r2 * pc;
+    pc = 1.0 / 40320.0 + r2 * pc;
+    pc = -1.0 / 720.0 + r2 * pc;
+    pc = 1.0 / 24.0 + r2 * pc;
+    pc = -1.0 / 2.0 + r2 * pc;
+    const double cr = 1.0 + r2 * pc;
+    switch ((int)(((int64_t)k) & 3)) {  // angle = r + k pi/2
+        case 0: s = sr; c = cr; break;
+        case 1: s = cr; c = -sr; break;
+        case 2: s = -sr; c = -cr; break;
+        default: s = -cr; c = sr; break;
+    }
+}
+__device__ inline void rope_rot(float& x, float& y, double c, double s) {
+#pragma clang fp contract(off)
+    const double xd = x, yd = y;
+    const double nx = xd * c - yd * s;
+    const double ny = yd * c + xd * s;
+    x = (float)nx;
+    y = (float)ny;
+}
+
+// The X = 16 / ELT values of a 16-byte piece, widened to float, and back (RNE).
+template <int DT>
+__device__ inline void piece_to_float(uint4 v, float* f) {
+    if constexpr (DT == PA_BF16) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = (float)b[j];
+    } else if constexpr (DT == PA_F16) {
+        const f16x8 h = __builtin_bit_cast(f16x8, v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = (float)h[j];
+    } else {
+        f[0] = __uint_as_float(v.x);
+        f[1] = __uint_as_float(v.y);
+        f[2] = __uint_as_float(v.z);
+        f[3] = __uint_as_float(v.w);
+    }
+}
+template <int DT>
+__device__ inline uint4 float_to_piece(const float* f) {
+    if constexpr (DT == PA_BF16) {
+        bf16x8 b;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = (__bf16)f[j];
+        return __builtin_bit_cast(uint4, b);
+    } else if constexpr (DT == PA_F16) {
+        f16x8 h;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) h[j] = (_Float16)f[j];
+        return __builtin_bit_cast(uint4, h);
+    } else {
+        return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+    }
+}
+
+// Rotate a row held as pieces: pieces[f] holds dims (4f + r) * X .. + X - 1 for
+// f < NF, so piece f and piece f + NF/2 hold the dims i and i + D/2 of the
+// same pairs (the fragments the QK product uses).
+template <int DT, int NF>
+__device__ inline void rope_fragments(uint4* pieces, int r, int pos, const double* w) {
+    constexpr int X = DT == PA_F32 ? 4 : 8;
+#pragma unroll
+    for (int f = 0; f < NF / 2; ++f) {
+        float x[X], y[X];
+        piece_to_float<DT>(pieces[f], x);
+        piece_to_float<DT>(pieces[f + NF / 2], y);
+#pragma unroll
+        for (int j = 0; j < X; ++j) {
+            double c, sn;
+            rope_cs(w[(4 * f + r) * X + j], pos, c, sn);
+            rope_rot(x[j], y[j], c, sn);
+        }
+        pieces[f] = float_to_piece<DT>(x);
+        pieces[f + NF / 2] = float_to_piece<DT>(y);
     }
 }
 
@@ -695,6 +804,9 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row
         const uint8_t* qrow = a.q + col_offset<MQ>(a, s, kvh, row0, qc, D) * E;
 #pragma unroll
         for (int f = 0; f < C::kKFrag; ++f) qf[f] = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * r);
+        if constexpr (APPEND && DT != PA_F32) {  // fused rotation: 16-bit caches
+            if (a.rope) rope_fragments<DT, C::kKFrag>(qf, r, ctx - 1, a.rope_w);  // the token's position
+        }
     }
 
     f32x4 O[C::kVChunk];
@@ -736,6 +848,9 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row
                                                         : reinterpret_cast<const uint32_t*>(vn)[d])
                                               : 0u;
                 }
+            if constexpr (DT != PA_F32) {
+                if (a.rope) rope_fragments<DT, C::kKFrag>(k_sub, r, tl, a.rope_w);
+            }
         }
     }
 
@@ -915,12 +1030,12 @@ __device__ void store_new_rows(const DecodeArgs& a, int wi) {
 
     // Byte offset of row `row`'s slab in either pool and the token's place in
     // it, or -1 when the row has nothing to store.
-    auto locate = [&](int row, int& tt) -> int64_t {
+    auto locate = [&](int row, int& tt, int& pos) -> int64_t {
         if (row >= rows) return -1;
         const int sq = row / Hkv, g = row % Hkv;
         const int L = clamp_ctx(a.context_lens[sq], B, a.max_blocks);
         if (L == 0) return -1;
-        const int pos = L - 1;
+        pos = L - 1;
         const int pl = a.block_tables[(size_t)sq * a.max_blocks + pos / B];
         if ((unsigned)pl >= (unsigned)a.num_blocks) return -1;
         tt = pos % 16;
@@ -942,18 +1057,40 @@ __device__ void store_new_rows(const DecodeArgs& a, int wi) {
                            : reinterpret_cast<const uint32_t*>(vn)[64 * k + lane];
     }
 
-    // K: lane (kq, ki) holds piece ki of row r0 + kq.
+    // K: lane (kq, ki) holds piece ki of row r0 + kq.  With the rotary
+    // embedding, piece ki pairs with piece ki ^ KP/2 (dims i and i + D/2) of
+    // the same row, in lane lane ^ KP/2.
     {
-        int tt = 0;
-        const int64_t slab = locate(r0 + kq, tt);
+        int tt = 0, pos = 0;
+        const int64_t slab = locate(r0 + kq, tt, pos);
+        if (DT != PA_F32 && a.rope) {
+            uint4 pv;
+            pv.x = __shfl_xor(kv.x, KP / 2);
+            pv.y = __shfl_xor(kv.y, KP / 2);
+            pv.z = __shfl_xor(kv.z, KP / 2);
+            pv.w = __shfl_xor(kv.w, KP / 2);
+            const bool lo = ki < KP / 2;
+            uint4 pr[2] = {lo ? kv : pv, lo ? pv : kv};  // (dims i, dims i + D/2)
+            constexpr int X = 16 / E;
+            float x[X], y[X];
+            piece_to_float<DT>(pr[0], x);
+            piece_to_float<DT>(pr[1], y);
+#pragma unroll
+            for (int j = 0; j < X; ++j) {
+                double c, sn;
+                rope_cs(a.rope_w[(ki % (KP / 2)) * X + j], pos, c, sn);
+                rope_rot(x[j], y[j], c, sn);
+            }
+            kv = lo ? float_to_piece<DT>(x) : float_to_piece<DT>(y);
+        }
         if (slab >= 0) store_nt(a.k_cache_w + slab + (ki * 16 + tt) * 16, kv);
     }
     // V: element k of the lane is dim (64k) % D + lane of row r0 + 64k / D.
     constexpr int Y = 4 / E;
 #pragma unroll
     for (int q = 0; q < RPW; ++q) {
-        int tt = 0;
-        const int64_t slab = locate(r0 + q, tt);
+        int tt = 0, pos = 0;
+        const int64_t slab = locate(r0 + q, tt, pos);
         if (slab < 0) continue;
 #pragma unroll
         for (int k = q * D / 64; k < (q + 1) * D / 64; ++k) {
@@ -1091,7 +1228,65 @@ __global__ __launch_bounds__(kWriteThreads) void write_kernel(WriteArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- rotary embedding, standalone
+
+struct RopeArgs {
+    uint8_t* q;
+    uint8_t* k;
+    const int32_t* positions;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    double w[kMaxRopePairs];
+};
+
+// One workgroup per token; thread j rotates pair j % (D/2) of head j / (D/2),
+// over the q heads and then the k heads, in place.
+template <int DT>
+__global__ __launch_bounds__(kWriteThreads) void rope_kernel(RopeArgs a) {
+    constexpr int E = DT == PA_F32 ? 4 : 2;
+    const int t = blockIdx.x, D = a.head_dim, half = D / 2;
+    const int pos = a.positions[t];
+    const int pairs = (a.num_q_heads + a.num_kv_heads) * half;
+    for (int j = threadIdx.x; j < pairs; j += kWriteThreads) {
+        const int h = j / half, i = j % half;
+        uint8_t* row = h < a.num_q_heads ? a.q + ((size_t)t * a.num_q_heads + h) * (size_t)(D * E)
+                                         : a.k + ((size_t)t * a.num_kv_heads + (h - a.num_q_heads)) * (size_t)(D * E);
+        float x, y;
+        if constexpr (DT == PA_BF16) {
+            x = (float)reinterpret_cast<const __bf16*>(row)[i];
+            y = (float)reinterpret_cast<const __bf16*>(row)[i + half];
+        } else if constexpr (DT == PA_F16) {
+            x = (float)reinterpret_cast<const _Float16*>(row)[i];
+            y = (float)reinterpret_cast<const _Float16*>(row)[i + half];
+        } else {
+            x = reinterpret_cast<const float*>(row)[i];
+            y = reinterpret_cast<const float*>(row)[i + half];
+        }
+        double c, sn;
+        rope_cs(a.w[i], pos, c, sn);
+        rope_rot(x, y, c, sn);
+        if constexpr (DT == PA_BF16) {
+            reinterpret_cast<__bf16*>(row)[i] = (__bf16)x;
+            reinterpret_cast<__bf16*>(row)[i + half] = (__bf16)y;
+        } else if constexpr (DT == PA_F16) {
+            reinterpret_cast<_Float16*>(row)[i] = (_Float16)x;
+            reinterpret_cast<_Float16*>(row)[i + half] = (_Float16)y;
+        } else {
+            reinterpret_cast<float*>(row)[i] = x;
+            reinterpret_cast<float*>(row)[i + half] = y;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- host side
+
+// Rotary frequencies theta^(-2i/D) for i < D/2, in double.
+bool rope_frequencies(float theta, int D, double* w) {
+    if (!std::isfinite(theta) || theta <= 1.f || D / 2 > kMaxRopePairs) return false;
+    for (int i = 0; i < D / 2; ++i) w[i] = std::pow((double)theta, -2.0 * i / D);
+    return true;
+}
 
 std::atomic<int> g_cu_count[64];
 
@@ -1270,15 +1465,18 @@ int tokens_per_pair(int num_q_heads, const pa_cache_desc_t* cache) {
 // pa_attend (mode kModeMulti: query_start and max_query_len).
 pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
-                        int32_t max_query_len, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
-                        int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
-                        size_t workspace_bytes, int32_t num_workers, int mode, pa_stream_t stream) {
+                        int32_t max_query_len, float scale, float rope_theta, void* out, int32_t num_seqs,
+                        int32_t num_q_heads, int32_t max_blocks_per_seq, const pa_cache_desc_t* cache,
+                        void* workspace, size_t workspace_bytes, int32_t num_workers, int mode,
+                        pa_stream_t stream) {
     pa_status_t st = check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache);
     if (st != PA_OK) return st;
     const bool append = mode == kModeAppend, multi = mode == kModeMulti;
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
     if (multi && max_query_len < 0) return PA_ERR_INVALID_ARG;
+    double rope_w[kMaxRopePairs] = {};
+    if (rope_theta != 0.f && !rope_frequencies(rope_theta, cache->head_dim, rope_w)) return PA_ERR_INVALID_ARG;
     // nothing is touched, so empty tensors may pass null pointers
     if (num_seqs == 0 || (multi && max_query_len == 0)) return PA_OK;
     if (!q || !k_cache || !v_cache || !context_lens || !out) return PA_ERR_INVALID_ARG;
@@ -1324,6 +1522,8 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     a.cols = tpc * G;
     a.query_start = query_start;
     a.tpc = tpc;
+    a.rope = rope_theta != 0.f;
+    for (int i = 0; i < kMaxRopePairs; ++i) a.rope_w[i] = rope_w[i];
     // A run start costs about as much as streaming kRunCostBytes of K/V: count
     // it as that many units so that workers with many short runs get fewer blocks.
     const size_t unit_bytes = (size_t)cache->block_size * cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2) * 2;
@@ -1430,8 +1630,8 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
                          size_t workspace_bytes, int32_t num_workers, pa_stream_t stream) {
     return decode_impl(q, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_tables,
-                       context_lens, nullptr, 1, scale, out, num_seqs, num_q_heads, max_blocks_per_seq, cache,
-                       workspace, workspace_bytes, num_workers, kModeDecode, stream);
+                       context_lens, nullptr, 1, scale, 0.f, out, num_seqs, num_q_heads, max_blocks_per_seq,
+                       cache, workspace, workspace_bytes, num_workers, kModeDecode, stream);
 }
 
 pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -1440,7 +1640,7 @@ pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, c
                       const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes, int32_t num_workers,
                       pa_stream_t stream) {
     return decode_impl(q, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_tables,
-                       context_lens, query_start, max_query_len, scale, out, num_seqs, num_q_heads,
+                       context_lens, query_start, max_query_len, scale, 0.f, out, num_seqs, num_q_heads,
                        max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers, kModeMulti, stream);
 }
 
@@ -1449,9 +1649,47 @@ pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new
                              int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                              const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
                              int32_t num_workers, pa_stream_t stream) {
-    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, scale, out,
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, scale, 0.f, out,
                        num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers,
                        kModeAppend, stream);
+}
+
+pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                  float rope_theta, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                  int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
+                                  size_t workspace_bytes, int32_t num_workers, pa_stream_t stream) {
+    if (rope_theta == 0.f) return PA_ERR_INVALID_ARG;  // 0 means "no rotation" inside
+    if (cache && cache->dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // f32: pa_rope, then pa_decode_append
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, scale, rope_theta,
+                       out, num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes,
+                       num_workers, kModeAppend, stream);
+}
+
+pa_status_t pa_rope(void* q, void* k, const int32_t* positions, int32_t num_tokens, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype, float rope_theta, pa_stream_t stream) {
+    if (num_tokens < 0 || num_q_heads < 0 || num_kv_heads < 0) return PA_ERR_INVALID_ARG;
+    if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128) return PA_ERR_UNSUPPORTED;
+    RopeArgs a{};
+    if (!rope_frequencies(rope_theta, head_dim, a.w)) return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0 || num_q_heads + num_kv_heads == 0) return PA_OK;  // nothing is touched
+    if (!positions || !aligned(positions, 4) || (num_q_heads > 0 && (!q || !aligned(q, 16))) ||
+        (num_kv_heads > 0 && (!k || !aligned(k, 16))))
+        return PA_ERR_INVALID_ARG;
+    a.q = static_cast<uint8_t*>(q);
+    a.k = static_cast<uint8_t*>(k);
+    a.positions = positions;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    void* args[] = {&a};
+    const void* fn = dtype == PA_F32   ? reinterpret_cast<const void*>(&rope_kernel<PA_F32>)
+                     : dtype == PA_F16 ? reinterpret_cast<const void*>(&rope_kernel<PA_F16>)
+                                       : reinterpret_cast<const void*>(&rope_kernel<PA_BF16>);
+    hipError_t e = hipLaunchKernel(fn, dim3(num_tokens), dim3(kWriteThreads), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PA_OK : PA_ERR_HIP;
 }
 
 pa_status_t pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

@@ -146,6 +146,27 @@ def test_attend_workspace_sizes():
     assert L.pa_attend_workspace_bytes(S, 32, 256, ctypes.byref(d), -1) == 0
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(theta=1.0), INVALID), (dict(theta=float("nan")), INVALID), (dict(theta=0.0), INVALID),
+    (dict(D=96), UNSUPPORTED), (dict(dtype=5), UNSUPPORTED), (dict(pos=None), INVALID), (dict(q=A + 4), INVALID),
+    (dict(T=-1), INVALID), (dict(T=0, q=None, k=None, pos=None), OK), (dict(Hq=0, Hkv=0, q=None, k=None), OK),
+])
+def test_rope_rejects(kw, status):
+    b = dict(q=A, k=A, pos=A, T=4, Hq=4, Hkv=2, D=128, dtype=2, theta=10000.0)
+    b.update(kw)
+    assert pa.lib().pa_rope(b["q"], b["k"], b["pos"], b["T"], b["Hq"], b["Hkv"], b["D"], b["dtype"], b["theta"],
+                            None) == status
+
+
+@pytest.mark.parametrize("kw,status", [(dict(theta=0.0), INVALID), (dict(theta=0.5), INVALID),
+                                       (dict(dtype=0, theta=10000.0), UNSUPPORTED), (dict(S=0, theta=10000.0), OK)])
+def test_decode_rope_append_rejects(kw, status):
+    d = _desc(dtype=kw.get("dtype", 2))
+    S = kw.get("S", 2)
+    assert pa.lib().pa_decode_rope_append(A, A, A, A, A, A, A, 0.125, kw["theta"], A, S, 4, 3, ctypes.byref(d), A,
+                                          1 << 30, 64, None) == status
+
+
 def test_decode_zero_sequences_is_a_noop():
     assert _decode(_desc(), S=0) == OK
 
