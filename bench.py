@@ -198,6 +198,47 @@ def measure_attend(n, q_len, args, device):
                 query_rows_per_s=round(int(mc.query_start[-1]) * case.Hq / (us * 1e-6)))
 
 
+def measure_rope(n, theta, args, device):
+    """The decode step with the rotary embedding of q and the new K rows fused
+    in (pa_decode_rope_append), beside pa_rope + pa_decode_append, K steps back
+    to back each."""
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+    from paged_kv_decode_slot_amd import workloads as W
+
+    case = W.config_case(n)
+    layer_bytes = 2 * case.pool_numel * case.elt
+    layers = args.layers or max(2, math.ceil(2 * 2**30 / layer_bytes))
+    _steps, pools = setup_layers(case, layers, device, args.workers)
+    q = case.q.to(device)
+    kn, vn = case.k_new.to(device), case.v_new.to(device)
+    bt = torch.from_numpy(case.block_tables).to(device)
+    ctx = torch.from_numpy(case.context_lens).to(device)
+    pos = torch.clamp(ctx - 1, min=0).to(torch.int32)
+    out = torch.empty_like(q)
+    fused = [pa.prepare_decode_rope_append(q, kn, vn, kc, vc, bt, ctx, case.scale, theta, out,
+                                           num_workers=args.workers) for (kc, vc) in pools]
+    q2, kn2 = q.clone(), kn.clone()
+    appends = [pa.prepare_decode_append(q2, kn2, vn, kc, vc, bt, ctx, case.scale, out, num_workers=args.workers)
+               for (kc, vc) in pools]
+
+    def two(i):
+        q2.copy_(q)  # pa_rope works in place
+        kn2.copy_(kn)
+        pa.rope(q2, kn2, pos, theta)
+        appends[i]()
+
+    fused_ms = time_back_to_back(fused, args.steps, args.warmup)
+    two_ms = time_back_to_back([(lambda i=i: two(i)) for i in range(len(pools))], args.steps, args.warmup)
+    b = W.step_bytes(case)
+    us = fused_ms * 1e3 / args.steps
+    return dict(workload=W.CONFIGS[n]["name"], rope_theta=theta, us=round(us, 2),
+                gbs=round(b / (us * 1e-6) / 1e9, 1), frac_of_peak=round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                two_calls_us=round(two_ms * 1e3 / args.steps, 2),
+                two_calls_note="copies of q and k_new (pa_rope works in place), pa_rope, pa_decode_append")
+
+
 # Measured HBM traffic of the decode kernel (two rocprofv3 counter passes, scaled by a
 # plain copy of known size), kept with the hash of the source it was measured on.
 TRAFFIC_FILES = {(3, "fused"): "profiles/decode_append_kernel_C3_llama3-8b_bf16_counters.txt",
@@ -258,6 +299,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--attend-q", type=int, default=4,
                     help="also time pa_attend with this many query tokens per sequence (0: skip)")
+    ap.add_argument("--rope-theta", type=float, default=500000.0,
+                    help="also time the step with the rotary embedding fused in, at this base (0: skip)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -308,6 +351,11 @@ def main():
     attend = None
     if args.attend_q > 0:
         attend = measure_attend(args.config, args.attend_q, args, device)
+        torch.cuda.empty_cache()
+
+    rope = None
+    if args.rope_theta > 0:
+        rope = measure_rope(args.config, args.rope_theta, args, device)
         torch.cuda.empty_cache()
 
     cpu = None
@@ -367,6 +415,7 @@ def main():
                 "t_decode_us_per_launch_events": r2(main_res["t_decode_us_events"]),
             },
             "attend": attend,
+            "rope": rope,
             "other": other,
         },
     }

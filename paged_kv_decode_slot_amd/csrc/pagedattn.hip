@@ -234,13 +234,15 @@ struct DecodeArgs {
     const int32_t* query_start;  // several query tokens: [num_seqs + 1] query rows of each sequence
     int32_t chunk;        // several query tokens: this launch takes tokens [chunk*tpc, (chunk+1)*tpc) of each
     int32_t tpc;          // several query tokens: tokens per pair (16 / G)
-    int32_t rope;         // append: 1 = rotate q and the new K rows at position ctx - 1 first
-    double rope_w[kMaxRopePairs];  // rotary frequencies theta^(-2i/D), i < D/2
+    double rope_w[kMaxRopePairs];  // append with rotary embedding: frequencies theta^(-2i/D), i < D/2
 };
 
 // What a decode_kernel instantiation computes: one query token per sequence,
-// the same with the KV append fused in, or several query tokens per sequence.
-enum { kModeDecode = 0, kModeAppend = 1, kModeMulti = 2 };
+// the same with the KV append fused in, or several query tokens per sequence;
+// kModeAppendRope is the append with the rotary embedding of q and the new K
+// rows fused in as well (16-bit caches).
+enum { kModeDecode = 0, kModeAppend = 1, kModeMulti = 2, kModeAppendRope = 3 };
+constexpr bool mode_appends(int mode) { return mode == kModeAppend || mode == kModeAppendRope; }
 
 // Element offset (in q or out) of column c of pair (s, kvh).  One token per
 // sequence: head kvh*G + c of row s.  Several: the pair holds query rows
@@ -271,7 +273,7 @@ __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
 // L - n + i0 + rows; row0[s] is the query row of token i0, rows[s] the count
 // (0: no work for s in this launch).
 template <int B, bool MQ>
-__device__ void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, int32_t* row0, int32_t* rows,
+__device__ __attribute__((always_inline)) void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, int32_t* row0, int32_t* rows,
                              int32_t* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = a.num_seqs;
@@ -427,50 +429,42 @@ __device__ inline void put_v_row(uint4& v, int e, const uint32_t* vals) {
 // ---------------------------------------------------------------- rotary embedding
 
 // Rotary embedding, rotate-half pairing: dims i and i + D/2 turn by pos * w_i.
-// Everything runs in double with every operation spelled out (no
-// contraction, no library call whose code could differ between call sites),
-// and the result is rounded once to float, so every kernel that rotates
-// produces the same bits: the angle (up to 10^5 radians for the first pairs
-// at long contexts) is reduced by multiples of pi/2, and sin and cos of the
-// remainder r in [-pi/4, pi/4] come from their Taylor series to the r^17 and
-// r^16 terms (Horner form), whose remainder there is below 1e-18.
-__device__ inline void rope_cs(double w, int pos, double& c, double& s) {
+// Every operation is spelled out (no contraction, no library call whose code
+// could differ between call sites), so every kernel that rotates produces the
+// same bits.  The angle (up to 10^5 radians for the first pairs at long
+// contexts) is formed in double and reduced there by multiples of pi/2; sin
+// and cos of the remainder r in [-pi/4, pi/4] come from their Taylor series to
+// the r^11 and r^12 terms in float (Horner form; the remainder is below 2e-9,
+// under float's resolution there), and the rotation is single precision.
+__device__ inline void rope_cs(double w, int pos, float& c, float& s) {
 #pragma clang fp contract(off)
     constexpr double kHalfPi = 1.5707963267948966;
     const double ang = (double)pos * w;
     const double k = rint(ang * (1.0 / kHalfPi));
-    const double r = fma(-kHalfPi, k, ang);
-    const double r2 = r * r;
-    double ps = -1.0 / 1307674368000.0 + r2 * (1.0 / 355687428096000.0);
-    ps = 1.0 / 6227020800.0 + r2 * ps;
-    ps = -1.0 / 39916800.0 + r2 * ps;
-    ps = 1.0 / 362880.0 + r2 * ps;
-    ps = -1.0 / 5040.0 + r2 * ps;
-    ps = 1.0 / 120.0 + r2 * ps;
-    ps = -1.0 / 6.0 + r2 * ps;
-    const double sr = r + (r * r2) * ps;
-    double pc = -1.0 / 87178291200.0 + r2 * (1.0 / 20922789888000.0);
-    pc = 1.0 / 479001600.0 + r2 * pc;
-    pc = -1.0 / 3628800.0 + r2 * pc;
-    pc = 1.0 / 40320.0 + r2 * pc;
-    pc = -1.0 / 720.0 + r2 * pc;
-    pc = 1.0 / 24.0 + r2 * pc;
-    pc = -1.0 / 2.0 + r2 * pc;
-    const double cr = 1.0 + r2 * pc;
-    switch ((int)(((int64_t)k) & 3)) {  // angle = r + k pi/2
-        case 0: s = sr; c = cr; break;
-        case 1: s = cr; c = -sr; break;
-        case 2: s = -sr; c = -cr; break;
-        default: s = -cr; c = sr; break;
-    }
+    const float r = (float)fma(-kHalfPi, k, ang);
+    const float r2 = r * r;
+    float ps = -1.0f / 5040.0f + r2 * (1.0f / 362880.0f - r2 * (1.0f / 39916800.0f));
+    ps = 1.0f / 120.0f + r2 * ps;
+    ps = -1.0f / 6.0f + r2 * ps;
+    const float sr = r + (r * r2) * ps;
+    float pc = 1.0f / 40320.0f + r2 * (-1.0f / 3628800.0f + r2 * (1.0f / 479001600.0f));
+    pc = -1.0f / 720.0f + r2 * pc;
+    pc = 1.0f / 24.0f + r2 * pc;
+    pc = -0.5f + r2 * pc;
+    const float cr = 1.0f + r2 * pc;
+    // angle = r + q pi/2 with q = k mod 4: (sin, cos) is (sr, cr), (cr, -sr),
+    // (-sr, -cr) or (-cr, sr); selects rather than a branch on q.
+    const int q = (int)(((int64_t)k) & 3);
+    const float sa = (q & 1) ? cr : sr, ca = (q & 1) ? sr : cr;
+    s = (q & 2) ? -sa : sa;
+    c = ((q + 1) & 2) ? -ca : ca;
 }
-__device__ inline void rope_rot(float& x, float& y, double c, double s) {
+__device__ inline void rope_rot(float& x, float& y, float c, float s) {
 #pragma clang fp contract(off)
-    const double xd = x, yd = y;
-    const double nx = xd * c - yd * s;
-    const double ny = yd * c + xd * s;
-    x = (float)nx;
-    y = (float)ny;
+    const float nx = x * c - y * s;
+    const float ny = y * c + x * s;
+    x = nx;
+    y = ny;
 }
 
 // The X = 16 / ELT values of a 16-byte piece, widened to float, and back (RNE).
@@ -512,7 +506,7 @@ __device__ inline uint4 float_to_piece(const float* f) {
 // f < NF, so piece f and piece f + NF/2 hold the dims i and i + D/2 of the
 // same pairs (the fragments the QK product uses).
 template <int DT, int NF>
-__device__ inline void rope_fragments(uint4* pieces, int r, int pos, const double* w) {
+__device__ __attribute__((always_inline)) inline void rope_fragments(uint4* pieces, int r, int pos, const double* w) {
     constexpr int X = DT == PA_F32 ? 4 : 8;
 #pragma unroll
     for (int f = 0; f < NF / 2; ++f) {
@@ -521,13 +515,55 @@ __device__ inline void rope_fragments(uint4* pieces, int r, int pos, const doubl
         piece_to_float<DT>(pieces[f + NF / 2], y);
 #pragma unroll
         for (int j = 0; j < X; ++j) {
-            double c, sn;
+            float c, sn;
             rope_cs(w[(4 * f + r) * X + j], pos, c, sn);
             rope_rot(x[j], y[j], c, sn);
         }
         pieces[f] = float_to_piece<DT>(x);
         pieces[f + NF / 2] = float_to_piece<DT>(y);
     }
+}
+
+// The same rotation for up to 16 rows (columns of the QK product) held as
+// operand pieces, through a per-wave LDS buffer: the lanes spread over the
+// pairs of the rows that need it instead of each turning all of its own
+// pieces.  Lane (n, r) holds pieces[f] = dims (4f + r) * 8 .. + 7 of a row;
+// lanes with `has` put theirs in row `wrow` of the buffer, rows [0, nrows)
+// (a wave-uniform count) are rotated, and those lanes take back row `rrow`.
+// 16-bit types only.
+template <int DT, int D, int NF>
+__device__ __attribute__((always_inline)) inline void rope_rows_lds(uint4* pieces, int wrow, int rrow, bool has, int nrows,
+                                                                    int r, int pos, const double* w, uint8_t* buf) {
+    static_assert(DT != PA_F32, "16-bit rows");
+    const int lane = threadIdx.x & 63;
+    uint4* b = reinterpret_cast<uint4*>(buf);  // [row][D / 8] 16-byte units
+    if (has) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) b[wrow * (D / 8) + 4 * f + r] = pieces[f];
+    }
+    __builtin_amdgcn_wave_barrier();
+    typedef typename std::conditional<DT == PA_BF16, __bf16, _Float16>::type T;
+    T* e = reinterpret_cast<T*>(buf);
+    const int pairs = nrows * (D / 2);
+#pragma unroll 1
+    for (int p0 = 0; p0 < pairs; p0 += kWave) {
+        const int p = p0 + lane;
+        const int rw = p / (D / 2), i = p % (D / 2);
+        if (p < pairs) {
+            float x = (float)e[rw * D + i], y = (float)e[rw * D + i + D / 2];
+            float c, sn;
+            rope_cs(w[i], pos, c, sn);
+            rope_rot(x, y, c, sn);
+            e[rw * D + i] = (T)x;
+            e[rw * D + i + D / 2] = (T)y;
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (has) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) pieces[f] = b[rrow * (D / 8) + 4 * f + r];
+    }
+    __builtin_amdgcn_wave_barrier();
 }
 
 template <int DT, int D, int B>
@@ -564,6 +600,9 @@ struct MergeLds {
     float den[kMaxGroup];       // running sum of weights
     float rescale[kMaxGroup];   // factor applied to earlier chunks when the running max grows
 };
+// (Before a run's first tile is consumed, the area also holds the 16 rows of
+// Q being rotated: 16 x 128 16-bit values.)
+static_assert(sizeof(MergeLds) >= 16 * 128 * 2, "rotation buffer");
 
 // Lane x of the same 16-lane row, by DPP: quad_perm [1,0,3,2] (xor 1),
 // quad_perm [2,3,0,1] (xor 2), row_ror 4 and row_ror 8.
@@ -624,7 +663,7 @@ __device__ inline float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_offset
 // merge of up to PB parts costs one round trip to memory.  Only the first
 // `active` columns are stored (the rest pad the last token group).
 template <int DT, int D, int UPL, bool MQ>
-__device__ void merge_body(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int parts,
+__device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int parts,
                            int64_t wa, int first_slot, bool unit_runs, int64_t U, int64_t W, int unit0,
                            MergeLds& L) {
     constexpr int E = DT == PA_F32 ? 4 : 2;
@@ -742,7 +781,7 @@ __device__ void merge_body(const DecodeArgs& a, int s, int kvh, int row0, int ac
 }
 
 template <int DT, int D, bool MQ>
-__device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int64_t Fv, int nb,
+__device__ __attribute__((always_inline)) void merge_parts(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int64_t Fv, int nb,
                             int64_t U, int64_t W, MergeLds& L) {
     const bool unit_runs = W >= U;
     const int64_t wa = owner_of(F, U, W);
@@ -773,12 +812,13 @@ __device__ void merge_parts(const DecodeArgs& a, int s, int kvh, int row0, int a
 // positions up to ctx - rows + i; otherwise the columns are the G heads of
 // sequence s's one token, which sees positions up to ctx - 1.
 template <int DT, int D, int B, int MODE>
-__device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row0, int rows, int j0, int j1, int nb,
-                           int64_t F, int64_t Fv, int64_t U, int64_t W, int w, int slot, MergeLds& mlds) {
+__device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row0, int rows, int j0, int j1, int nb,
+                           int64_t F, int64_t Fv, int64_t U, int64_t W, int w, int slot, MergeLds& mlds,
+                           const double* rw) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
     constexpr int NBUF = PA_TILE_BUFFERS;
-    constexpr bool APPEND = MODE == kModeAppend, MQ = MODE == kModeMulti;
+    constexpr bool APPEND = mode_appends(MODE), MQ = MODE == kModeMulti, ROPE = MODE == kModeAppendRope;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;  // this lane's column (and row within a 16-row piece)
     const int r = lane >> 4;  // this lane's group of 4 rows / k-range
@@ -804,9 +844,6 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row
         const uint8_t* qrow = a.q + col_offset<MQ>(a, s, kvh, row0, qc, D) * E;
 #pragma unroll
         for (int f = 0; f < C::kKFrag; ++f) qf[f] = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * r);
-        if constexpr (APPEND && DT != PA_F32) {  // fused rotation: 16-bit caches
-            if (a.rope) rope_fragments<DT, C::kKFrag>(qf, r, ctx - 1, a.rope_w);  // the token's position
-        }
     }
 
     f32x4 O[C::kVChunk];
@@ -848,9 +885,6 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row
                                                         : reinterpret_cast<const uint32_t*>(vn)[d])
                                               : 0u;
                 }
-            if constexpr (DT != PA_F32) {
-                if (a.rope) rope_fragments<DT, C::kKFrag>(k_sub, r, tl, a.rope_w);
-            }
         }
     }
 
@@ -940,17 +974,30 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row
     // always fall in the peeled tail, so it never pays for masking.
     constexpr int kMasked = MQ ? C::kSub + 1 : C::kSub;
     constexpr int kTail = (NBUF - 1 > kMasked ? NBUF - 1 : kMasked);
+    // With the rotary embedding fused in, Q and the new K row are rotated (at
+    // the token's position, ctx - 1) once the first tiles are on their way, so
+    // the rotation overlaps their latency instead of delaying their issue.
+    auto rotate_inputs = [&]() {
+        if constexpr (ROPE) {
+            uint8_t* lbuf = reinterpret_cast<uint8_t*>(&mlds);  // free until the merge
+            // Only the active columns are turned; padding columns take column 0's result.
+            rope_rows_lds<DT, D, C::kKFrag>(qf, n, qc, true, active, r, ctx - 1, rw, lbuf);
+            if (owns_new) rope_rows_lds<DT, D, C::kKFrag>(k_sub, 0, 0, n == tt, 1, r, tl, rw, lbuf);
+        }
+    };
     Tile<DT, D, B> buf[NBUF];
     if (ntiles < NBUF) {
 #pragma unroll
         for (int i = 0; i < NBUF; ++i)
             if (i < ntiles) issue(i, buf[i]);
+        rotate_inputs();
 #pragma unroll
         for (int i = 0; i < NBUF; ++i)
             if (i < ntiles) consume(i, buf[i], true);
     } else {
 #pragma unroll
         for (int i = 0; i < NBUF - 1; ++i) issue(i, buf[i]);
+        rotate_inputs();
         int tau0 = 0;
         for (; tau0 + NBUF - 1 + kTail < ntiles; tau0 += NBUF) {
 #pragma unroll
@@ -1015,8 +1062,8 @@ __device__ void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row
 // partial lines stream out instead of sitting dirty in L2 costs the reads
 // around them less.  A row with no context, or whose block id or length lies
 // outside the table or pool, is skipped.
-template <int DT, int D, int B>
-__device__ void store_new_rows(const DecodeArgs& a, int wi) {
+template <int DT, int D, int B, bool ROPE>
+__device__ __attribute__((always_inline)) void store_new_rows(const DecodeArgs& a, int wi, const double* rw) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
     constexpr int KP = D * E / 16;  // 16-byte pieces per row
@@ -1063,7 +1110,7 @@ __device__ void store_new_rows(const DecodeArgs& a, int wi) {
     {
         int tt = 0, pos = 0;
         const int64_t slab = locate(r0 + kq, tt, pos);
-        if (DT != PA_F32 && a.rope) {
+        if constexpr (ROPE) {
             uint4 pv;
             pv.x = __shfl_xor(kv.x, KP / 2);
             pv.y = __shfl_xor(kv.y, KP / 2);
@@ -1077,8 +1124,8 @@ __device__ void store_new_rows(const DecodeArgs& a, int wi) {
             piece_to_float<DT>(pr[1], y);
 #pragma unroll
             for (int j = 0; j < X; ++j) {
-                double c, sn;
-                rope_cs(a.rope_w[(ki % (KP / 2)) * X + j], pos, c, sn);
+                float c, sn;
+                rope_cs(rw[(ki % (KP / 2)) * X + j], pos, c, sn);
                 rope_rot(x[j], y[j], c, sn);
             }
             kv = lo ? float_to_piece<DT>(x) : float_to_piece<DT>(y);
@@ -1113,14 +1160,26 @@ constexpr size_t kDecodeStaticLds = sizeof(MergeLds) * kWavesPerGroup + sizeof(i
 template <int DT, int D, int B, int MODE>
 __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
     using C = Cfg<DT, D, B>;
-    constexpr bool APPEND = MODE == kModeAppend, MQ = MODE == kModeMulti;
+    constexpr bool APPEND = mode_appends(MODE), MQ = MODE == kModeMulti;
     // ctx[num_seqs], pre[num_seqs + 1]; several query tokens: row0[num_seqs], rows[num_seqs]
     extern __shared__ int32_t s_lds[];
     __shared__ int32_t s_wave_tot[kWavesPerGroup];
     __shared__ MergeLds s_merge[kWavesPerGroup];
+    // Rotary frequencies in LDS: lanes index them by their own dims, and a
+    // lane-dependent index into the argument block would copy it to scratch.
+    constexpr bool ROPE = MODE == kModeAppendRope;
+    __shared__ double s_rope_w[ROPE ? kMaxRopePairs : 1];
+    if constexpr (ROPE) {
+        if (threadIdx.x == 0) {  // one lane, constant indices: scalar loads of the argument block
+#pragma unroll
+            for (int i = 0; i < kMaxRopePairs; ++i) s_rope_w[i] = a.rope_w[i];
+        }
+        __syncthreads();
+    }
     if constexpr (APPEND) {
         if ((int)blockIdx.x >= a.attn_groups) {
-            store_new_rows<DT, D, B>(a, (blockIdx.x - a.attn_groups) * kWavesPerGroup + (threadIdx.x >> 6));
+            store_new_rows<DT, D, B, ROPE>(a, (blockIdx.x - a.attn_groups) * kWavesPerGroup + (threadIdx.x >> 6),
+                                           s_rope_w);
             return;
         }
     }
@@ -1178,7 +1237,7 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         const int rows = MQ ? __builtin_amdgcn_readfirstlane(s_rows[s]) : 1;
         if (j1 > j0)  // a range that ends inside the leading units holds no block
             attend_run<DT, D, B, MODE>(a, s, kvh, ctx, row0, rows, j0, j1, nb, Fv + cost, Fv, U, W, w,
-                                       u == start ? 0 : 1, s_merge[threadIdx.x >> 6]);
+                                       u == start ? 0 : 1, s_merge[threadIdx.x >> 6], s_rope_w);
         u += jv1 - jv0;
     }
 }
@@ -1263,7 +1322,7 @@ __global__ __launch_bounds__(kWriteThreads) void rope_kernel(RopeArgs a) {
             x = reinterpret_cast<const float*>(row)[i];
             y = reinterpret_cast<const float*>(row)[i + half];
         }
-        double c, sn;
+        float c, sn;
         rope_cs(a.w[i], pos, c, sn);
         rope_rot(x, y, c, sn);
         if constexpr (DT == PA_BF16) {
@@ -1416,7 +1475,7 @@ size_t decode_dynamic_lds(int num_seqs, bool multi) {
 template <int DT, int D, int B, int MODE>
 hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stream) {
     using C = Cfg<DT, D, B>;
-    constexpr bool APPEND = MODE == kModeAppend;
+    constexpr bool APPEND = mode_appends(MODE);
     const int groups = (plan.workers + kWavesPerGroup - 1) / kWavesPerGroup;
     if (groups == 0) return hipSuccess;
     DecodeArgs args_copy = a;
@@ -1471,7 +1530,7 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
                         pa_stream_t stream) {
     pa_status_t st = check_decode_shapes(num_seqs, num_q_heads, max_blocks_per_seq, cache);
     if (st != PA_OK) return st;
-    const bool append = mode == kModeAppend, multi = mode == kModeMulti;
+    const bool append = mode_appends(mode), multi = mode == kModeMulti;
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
     if (multi && max_query_len < 0) return PA_ERR_INVALID_ARG;
@@ -1522,7 +1581,6 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     a.cols = tpc * G;
     a.query_start = query_start;
     a.tpc = tpc;
-    a.rope = rope_theta != 0.f;
     for (int i = 0; i < kMaxRopePairs; ++i) a.rope_w[i] = rope_w[i];
     // A run start costs about as much as streaming kRunCostBytes of K/V: count
     // it as that many units so that workers with many short runs get fewer blocks.
@@ -1537,6 +1595,15 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
 
     hipStream_t sm = static_cast<hipStream_t>(stream);
     if (!multi) {
+        if (mode == kModeAppendRope) {
+            if (cache->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+            const hipError_t e = cache->dtype == PA_F16
+                                     ? dispatch_decode<PA_F16, kModeAppendRope>(a, plan, cache->head_dim,
+                                                                                 cache->block_size, sm)
+                                     : dispatch_decode<PA_BF16, kModeAppendRope>(a, plan, cache->head_dim,
+                                                                                  cache->block_size, sm);
+            return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+        }
         const hipError_t e = append ? dispatch_dtype<kModeAppend>(a, plan, cache, sm)
                                     : dispatch_dtype<kModeDecode>(a, plan, cache, sm);
         return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -1663,7 +1730,7 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
     if (cache && cache->dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // f32: pa_rope, then pa_decode_append
     return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, scale, rope_theta,
                        out, num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes,
-                       num_workers, kModeAppend, stream);
+                       num_workers, kModeAppendRope, stream);
 }
 
 pa_status_t pa_rope(void* q, void* k, const int32_t* positions, int32_t num_tokens, int32_t num_q_heads,
