@@ -195,7 +195,8 @@ def measure_attend(n, q_len, args, device):
     b = W.attend_bytes(mc)
     return dict(workload=W.CONFIGS[n]["name"], query_tokens_per_seq=q_len, us=round(us, 2),
                 bytes=b, gbs=round(b / (us * 1e-6) / 1e9, 1), frac_of_peak=round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-                query_rows_per_s=round(int(mc.query_start[-1]) * case.Hq / (us * 1e-6)))
+                query_rows_per_s=round(int(mc.query_start[-1]) * case.Hq / (us * 1e-6)),
+                traffic=measured_traffic(n, f"attend{q_len}"))
 
 
 def measure_rope(n, theta, args, device):
@@ -235,6 +236,7 @@ def measure_rope(n, theta, args, device):
     us = fused_ms * 1e3 / args.steps
     return dict(workload=W.CONFIGS[n]["name"], rope_theta=theta, us=round(us, 2),
                 gbs=round(b / (us * 1e-6) / 1e9, 1), frac_of_peak=round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                traffic=measured_traffic(n, "rope"),
                 two_calls_us=round(two_ms * 1e3 / args.steps, 2),
                 two_calls_note="copies of q and k_new (pa_rope works in place), pa_rope, pa_decode_append")
 
@@ -242,7 +244,9 @@ def measure_rope(n, theta, args, device):
 # Measured HBM traffic of the decode kernel (two rocprofv3 counter passes, scaled by a
 # plain copy of known size), kept with the hash of the source it was measured on.
 TRAFFIC_FILES = {(3, "fused"): "profiles/decode_append_kernel_C3_llama3-8b_bf16_counters.txt",
-                 (3, "decode"): "profiles/decode_kernel_C3_llama3-8b_bf16_counters.txt"}
+                 (3, "decode"): "profiles/decode_kernel_C3_llama3-8b_bf16_counters.txt",
+                 (3, "attend4"): "profiles/attend_kernel_C3_llama3-8b_4tokens_bf16_counters.txt",
+                 (3, "rope"): "profiles/decode_rope_append_kernel_C3_llama3-8b_bf16_counters.txt"}
 KERNEL_SOURCE = "paged_kv_decode_slot_amd/csrc/pagedattn.hip"
 
 
