@@ -54,6 +54,12 @@ def _load():
         lib.oracle_round.restype = I
         lib.oracle_widen.argtypes = [P, I64, I, P]
         lib.oracle_widen.restype = None
+        lib.oracle_pool_init.argtypes = [P, P, I]
+        lib.oracle_pool_init.restype = None
+        lib.oracle_assign_slots.argtypes = [P, P, P, P, P, P, I, I, I]
+        lib.oracle_assign_slots.restype = I
+        lib.oracle_release_seqs.argtypes = [P, I, P, P, P, P, I, I, I, I]
+        lib.oracle_release_seqs.restype = I
         _lib = lib
     return _lib
 
@@ -192,3 +198,49 @@ def decode_case(case, k_pool=None, v_pool=None, pairs=None, threads=None) -> np.
         k_pool, v_pool = build_pools(case)
     return decode(case.q, k_pool, v_pool, case.block_tables, case.context_lens, case.scale,
                   Hkv=case.Hkv, B=case.B, pairs=pairs, threads=threads)
+
+
+# --- block pool: a stack of free block ids and its state record (see pa_oracle.c) ---
+
+def pool_init(capacity: int, num_free: int):
+    """A fresh pool: (free_ids int32[capacity], state int32[8]) with ids 0 .. num_free-1 free."""
+    assert 0 <= num_free <= capacity
+    free_ids = np.full(capacity, -7, dtype=np.int32)  # entries at and above top are never read
+    state = np.zeros(8, dtype=np.int32)
+    _load().oracle_pool_init(_ptr(free_ids), _ptr(state), num_free)
+    return free_ids, state
+
+
+def assign_slots(context_lens: np.ndarray, query_start, block_tables: np.ndarray, free_ids: np.ndarray,
+                 state: np.ndarray, *, B: int) -> np.ndarray:
+    """Blocks for each sequence's new tokens (block_tables and state updated in
+    place) and their slots, int64 [rows].  query_start None: one token per sequence."""
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = ctx.shape[0]
+    assert block_tables.dtype == np.int32 and block_tables.flags["C_CONTIGUOUS"] and block_tables.shape[0] == S
+    assert free_ids.dtype == np.int32 and state.dtype == np.int32 and state.shape == (8,)
+    if query_start is None:
+        qs, rows = None, S
+    else:
+        qs = np.ascontiguousarray(query_start, dtype=np.int32)
+        assert qs.shape == (S + 1,)
+        rows = int(qs[-1])
+    slots = np.empty(rows, dtype=np.int64)
+    rc = _load().oracle_assign_slots(_ptr(ctx), None if qs is None else _ptr(qs), _ptr(block_tables),
+                                     _ptr(free_ids), _ptr(state), _ptr(slots), S, block_tables.shape[1], B)
+    if rc:
+        raise ValueError("oracle_assign_slots: bad argument")
+    return slots
+
+
+def release_seqs(seq_ids, context_lens: np.ndarray, block_tables: np.ndarray, free_ids: np.ndarray,
+                 state: np.ndarray, *, B: int) -> None:
+    """Return the listed sequences' blocks to the stack (in place); the stack holds at most len(free_ids)."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    S = ctx.shape[0]
+    assert block_tables.dtype == np.int32 and block_tables.flags["C_CONTIGUOUS"] and block_tables.shape[0] == S
+    rc = _load().oracle_release_seqs(_ptr(ids), ids.shape[0], _ptr(ctx), _ptr(block_tables), _ptr(free_ids),
+                                     _ptr(state), S, block_tables.shape[1], B, free_ids.shape[0])
+    if rc:
+        raise ValueError("oracle_release_seqs: bad argument")

@@ -1,6 +1,6 @@
 /*
- * Plain, slow, float64 CPU oracle for paged-KV decode attention and for the
- * KV-append slot write.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check
+ * Plain, slow, float64 CPU oracle for paged-KV decode attention, for the
+ * KV-append slot write and for the block pool that hands out the slots.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check
  * and the CPU-baseline leg of the benchmark call it; the library never does.
  * It shares no code, header or constant with the HIP library.
  *
@@ -421,4 +421,107 @@ int oracle_round(const double* in, int64_t n, int dtype, double* out) {
 /* Exposes the element widening on its own, so it can be checked against other converters. */
 void oracle_widen(const void* src, int64_t n, int dtype, double* dst) {
     for (int64_t i = 0; i < n; ++i) dst[i] = widen(src, (size_t)i, dtype);
+}
+
+/*
+ * Block pool (ForgeLLM README, feature list: physical KV blocks behind
+ * per-request logical block tables, worst-case admission reservation,
+ * reclamation and capacity errors; LLM-Inference-Engine README, the "why
+ * paged KV cache" paragraph and the request-journey figure: fixed-size blocks
+ * from a preallocated pool, handed to a request on demand as it grows).
+ *
+ * The pool is a stack of free block ids, free_ids[0 .. top), the top at
+ * index top - 1, and a state record of 8 int32:
+ *   [0] top: free blocks        [1] sequences refused for lack of blocks
+ *   [2] lowest top since init   [3] release calls refused (stack would overflow)
+ *   [4..7] zero between calls
+ *
+ * init: the ids 0 .. num_free - 1, stacked so that pops yield them in
+ *   increasing order.
+ * assign: sequences are taken in order.  Sequence s has L = context_lens[s]
+ *   positions after the call, the newest n of them new (n = query_start[s+1] -
+ *   query_start[s], or 1 without query_start), so it already holds
+ *   have = ceil((L - n) / B) blocks and needs ceil(L / B) - have more.  A
+ *   sequence needing none is always served; otherwise it is served when the
+ *   stack still holds what it needs and no earlier sequence was refused, and
+ *   takes that many ids off the top, the first one popped becoming its block
+ *   `have`.  Each new token's slot is block_table[s][p / B] * B + p % B for its
+ *   position p = L - n + i; a refused sequence's tokens (and positions below
+ *   0) get -1 and its table is left alone.
+ * release: the listed sequences (in list order; ids outside [0, S) hold
+ *   nothing) push blocks 0 .. ceil(L / B) - 1 of their tables, in that order,
+ *   and those table entries become -1; if the stack would then hold more than
+ *   `capacity` ids, nothing changes and state[3] counts the refusal.
+ */
+void oracle_pool_init(int32_t* free_ids, int32_t* state, int32_t num_free) {
+    for (int32_t i = 0; i < num_free; ++i) free_ids[i] = num_free - 1 - i;
+    for (int k = 0; k < 8; ++k) state[k] = 0;
+    state[0] = num_free;
+    state[2] = num_free;
+}
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int oracle_assign_slots(const int32_t* ctx, const int32_t* qs, int32_t* bt, const int32_t* free_ids, int32_t* state,
+                        int64_t* slots, int S, int M, int B) {
+    if (S < 0 || M < 0 || B <= 0) return 1;
+    int refusing = 0;
+    for (int s = 0; s < S; ++s) {
+        int64_t L = ctx[s];
+        if (L < 0) L = 0;
+        if (L > (int64_t)M * B) L = (int64_t)M * B;
+        const int64_t row0 = qs ? qs[s] : s;
+        const int64_t n = qs ? qs[s + 1] - qs[s] : 1;
+        const int64_t first = L - n;
+        const int64_t have = first > 0 ? ceil_div(first, B) : 0;
+        const int64_t need = ceil_div(L, B) - have;
+        int served = 1;
+        if (need > 0) {
+            if (refusing || need > state[0]) {
+                refusing = 1;
+                served = 0;
+                state[1] += 1;
+            } else {
+                for (int64_t k = 0; k < need; ++k) {
+                    state[0] -= 1;
+                    bt[(size_t)s * M + have + k] = free_ids[state[0]];
+                }
+            }
+        }
+        for (int64_t i = 0; i < n; ++i) {
+            const int64_t p = first + i;
+            slots[row0 + i] = (served && p >= 0) ? (int64_t)bt[(size_t)s * M + p / B] * B + p % B : -1;
+        }
+    }
+    if (state[0] < state[2]) state[2] = state[0];
+    return 0;
+}
+
+int oracle_release_seqs(const int32_t* ids, int R, const int32_t* ctx, int32_t* bt, int32_t* free_ids, int32_t* state,
+                        int S, int M, int B, int32_t capacity) {
+    if (R < 0 || S < 0 || M < 0 || B <= 0) return 1;
+    int64_t total = 0;
+    for (int r = 0; r < R; ++r) {
+        const int s = ids[r];
+        if (s < 0 || s >= S) continue;
+        int64_t L = ctx[s] < 0 ? 0 : ctx[s];
+        if (L > (int64_t)M * B) L = (int64_t)M * B;
+        total += ceil_div(L, B);
+    }
+    if (state[0] + total > capacity) {
+        state[3] += 1;
+        return 0;
+    }
+    for (int r = 0; r < R; ++r) {
+        const int s = ids[r];
+        if (s < 0 || s >= S) continue;
+        int64_t L = ctx[s] < 0 ? 0 : ctx[s];
+        if (L > (int64_t)M * B) L = (int64_t)M * B;
+        for (int64_t j = 0; j < ceil_div(L, B); ++j) {
+            free_ids[state[0]] = bt[(size_t)s * M + j];
+            state[0] += 1;
+            bt[(size_t)s * M + j] = -1;
+        }
+    }
+    return 0;
 }
