@@ -54,14 +54,15 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, Hq not a multiple of Hkv */
     PA_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
     PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-    PA_ERR_HIP = 4          /* a HIP runtime call or a launch failed */
+    PA_ERR_HIP = 4,         /* a HIP runtime call or a launch failed */
+    PA_ERR_CAPACITY = 5     /* the block pool cannot promise what an admission asks for */
 } pa_status_t;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
@@ -239,6 +240,109 @@ size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32
 
 /* Static, human-readable name of a status. */
 const char* pa_status_string(pa_status_t status);
+
+/*
+ * Block pool (ForgeLLM README, feature list: physical KV blocks behind
+ * per-request logical block tables, worst-case admission reservation,
+ * reclamation, capacity errors and occupancy/byte telemetry;
+ * LLM-Inference-Engine README, the "why paged KV cache" paragraph and the
+ * request-journey figure: fixed-size blocks from a preallocated pool, handed
+ * to a request on demand as it grows).
+ *
+ * The free blocks are a stack of ids in device memory, free_ids[0 .. top),
+ * with the top at index top - 1, and a device state record pool_state of 8
+ * int32 (8-byte aligned):
+ *   [0] top: free blocks          [1] sequences refused for lack of blocks
+ *   [2] lowest top since init     [3] releases refused (the stack would overflow)
+ *   [4..7] internal, zero between calls
+ * `capacity` is the length of free_ids.  The calls below keep the stack and
+ * the tables on the device and run on `stream` with no host synchronisation;
+ * calls on one pool must not overlap (use one stream).  Every index they form
+ * is bounded by capacity, the table width and num_tokens, so malformed device
+ * values give unspecified ids, never an access outside those arrays.
+ */
+
+/* Stack the ids 0 .. num_free - 1 so that pops yield them in increasing
+ * order; the rest of free_ids becomes -1 and the counters start at zero.
+ * 0 <= num_free <= capacity. */
+pa_status_t pa_pool_init(int32_t* free_ids, int32_t* pool_state, int32_t num_free, int32_t capacity,
+                         pa_stream_t stream);
+
+/*
+ * Give each sequence's new tokens their blocks and slots.  Sequence s has
+ * L = context_lens[s] positions after this step, the newest
+ * n = query_start[s+1] - query_start[s] of them new (n = 1 for every sequence
+ * when query_start is NULL, and then num_tokens = num_seqs); it already holds
+ * blocks 0 .. ceil((L - n) / B) - 1 of its table row and needs the blocks up
+ * to ceil(L / B) - 1.  Sequences are served in order: one needing no block
+ * is always served; one needing k blocks is served when k ids remain and no
+ * earlier sequence was refused, and pops them, the first popped becoming its
+ * lowest new block.  Row query_start[s] + i (position p = L - n + i) gets
+ * slot_mapping = block_tables[s][p / B] * B + p % B, ready for pa_write_kv;
+ * a refused sequence's rows get -1, its table row is left alone and
+ * pool_state[1] counts it.
+ *   context_lens : int32 [num_seqs], device; query_start : int32 [num_seqs + 1]
+ *       non-decreasing from 0 to num_tokens, device, or NULL
+ *   block_tables : int32 [num_seqs][max_blocks_per_seq], device, updated
+ *   slot_mapping : int64 [num_tokens], device, written
+ *   block_size   : B, the pool's tokens per block
+ * Preconditions (unchecked): L <= max_blocks_per_seq * B (longer lengths are
+ * clamped), n >= 0.  Rows whose position would be below 0 get -1.
+ */
+pa_status_t pa_assign_slots(const int32_t* context_lens, const int32_t* query_start, int32_t* block_tables,
+                            const int32_t* free_ids, int32_t* pool_state, int64_t* slot_mapping, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t block_size, int32_t num_tokens, int32_t capacity,
+                            pa_stream_t stream);
+
+/*
+ * Reclaim finished sequences: for r = 0 .. num_release - 1 in order, sequence
+ * seq_ids[r] pushes blocks 0 .. ceil(context_lens[s] / B) - 1 of its table
+ * row, in that order, and those entries become -1.  Ids outside
+ * [0, num_seqs) hold nothing.  If the stack would then exceed capacity,
+ * nothing changes and pool_state[3] counts the refusal.
+ * Precondition (unchecked): the ids are distinct.
+ */
+pa_status_t pa_release_seqs(const int32_t* seq_ids, int32_t num_release, const int32_t* context_lens,
+                            int32_t* block_tables, int32_t* free_ids, int32_t* pool_state, int32_t num_seqs,
+                            int32_t max_blocks_per_seq, int32_t block_size, int32_t capacity, pa_stream_t stream);
+
+/*
+ * Host-side admission accounting, worst case: a request is admitted only if
+ * the blocks for its largest possible length (prompt plus the most tokens it
+ * may generate) fit beside every admitted request's, so the device pool can
+ * never run dry for admitted requests.  Plain host memory, no GPU calls.
+ */
+typedef struct pa_pool_acct {
+    int64_t num_blocks;           /* blocks in the pool */
+    int64_t block_size;           /* tokens per block */
+    int64_t bytes_per_block;      /* K and V bytes of one block, all kv-heads */
+    int64_t reserved_blocks;      /* promised to admitted requests */
+    int64_t peak_reserved_blocks;
+    int64_t admitted;             /* admitted and not yet retired */
+    int64_t refused;              /* admissions refused with PA_ERR_CAPACITY */
+} pa_pool_acct_t;
+
+pa_status_t pa_acct_init(pa_pool_acct_t* acct, int64_t num_blocks, int32_t block_size, int64_t bytes_per_block);
+/* Reserve ceil(max_tokens / block_size) blocks, or PA_ERR_CAPACITY (nothing reserved). */
+pa_status_t pa_acct_admit(pa_pool_acct_t* acct, int64_t max_tokens);
+/* Give back an admitted request's reservation (the same max_tokens). */
+pa_status_t pa_acct_retire(pa_pool_acct_t* acct, int64_t max_tokens);
+
+/* Occupancy and bytes, from the accounting and a host copy of pool_state. */
+typedef struct pa_pool_telemetry {
+    int64_t capacity_blocks, free_blocks, used_blocks, peak_used_blocks;
+    int64_t capacity_bytes, used_bytes;
+    int64_t reserved_blocks, peak_reserved_blocks, admitted;
+    int64_t tokens_stored; /* as given: the sum of the live sequences' lengths */
+    int64_t empty_slots;   /* slots of used blocks that hold no token */
+    double occupancy;      /* used_blocks / capacity_blocks */
+    int64_t refused_admissions, refused_sequences, refused_releases;
+} pa_pool_telemetry_t;
+
+/* state_host: the 8 int32 of pool_state copied to the host.  PA_ERR_INVALID_ARG
+ * when the figures contradict each other (more tokens than used slots). */
+pa_status_t pa_pool_telemetry(const pa_pool_acct_t* acct, const int32_t* state_host, int64_t tokens_stored,
+                              pa_pool_telemetry_t* out);
 
 /* PA_ABI_VERSION of the built library. */
 int32_t pa_abi_version(void);

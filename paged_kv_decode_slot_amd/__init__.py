@@ -7,7 +7,17 @@ seeded workload generator used by the tests and the benchmark.
 """
 from .binding import (  # noqa: F401
     CacheDesc,
+    CapacityError,
     PagedAttnError,
+    PoolAcct,
+    acct_admit,
+    acct_init,
+    acct_retire,
+    assign_slots,
+    pool_init,
+    pool_telemetry,
+    prepare_assign_slots,
+    release_seqs,
     attend,
     cache_desc,
     cache_shapes,

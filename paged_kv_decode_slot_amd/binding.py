@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
                                                            "libpagedattn.so")
 
-PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_CAPACITY = range(6)
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _ELT = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
 
@@ -31,6 +31,13 @@ EXPORTS = (
     "pa_decode_rope_append",
     "pa_decode_workspace_bytes",
     "pa_decode_workspace_bytes_ex",
+    "pa_pool_init",
+    "pa_assign_slots",
+    "pa_release_seqs",
+    "pa_acct_init",
+    "pa_acct_admit",
+    "pa_acct_retire",
+    "pa_pool_telemetry",
     "pa_status_string",
     "pa_abi_version",
 )
@@ -44,6 +51,28 @@ class CacheDesc(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
     ]
+
+
+class PoolAcct(ctypes.Structure):
+    """pa_pool_acct_t: host-side worst-case admission accounting."""
+    _fields_ = [(n, ctypes.c_int64) for n in ("num_blocks", "block_size", "bytes_per_block", "reserved_blocks",
+                                              "peak_reserved_blocks", "admitted", "refused")]
+
+
+class PoolTelemetry(ctypes.Structure):
+    """pa_pool_telemetry_t."""
+    _fields_ = ([(n, ctypes.c_int64) for n in ("capacity_blocks", "free_blocks", "used_blocks", "peak_used_blocks",
+                                               "capacity_bytes", "used_bytes", "reserved_blocks",
+                                               "peak_reserved_blocks", "admitted", "tokens_stored", "empty_slots")]
+                + [("occupancy", ctypes.c_double)]
+                + [(n, ctypes.c_int64) for n in ("refused_admissions", "refused_sequences", "refused_releases")])
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _t in self._fields_}
+
+
+class CapacityError(RuntimeError):
+    """An admission the pool cannot promise (PA_ERR_CAPACITY)."""
 
 
 class PagedAttnError(RuntimeError):
@@ -89,6 +118,21 @@ def lib() -> ctypes.CDLL:
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_abi_version.argtypes = []
         L.pa_abi_version.restype = I32
+        L.pa_pool_init.argtypes = [P, P, I32, I32, P]
+        L.pa_pool_init.restype = ctypes.c_int
+        L.pa_assign_slots.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, P]
+        L.pa_assign_slots.restype = ctypes.c_int
+        L.pa_release_seqs.argtypes = [P, I32, P, P, P, P, I32, I32, I32, I32, P]
+        L.pa_release_seqs.restype = ctypes.c_int
+        AP = ctypes.POINTER(PoolAcct)
+        L.pa_acct_init.argtypes = [AP, ctypes.c_int64, I32, ctypes.c_int64]
+        L.pa_acct_init.restype = ctypes.c_int
+        L.pa_acct_admit.argtypes = [AP, ctypes.c_int64]
+        L.pa_acct_admit.restype = ctypes.c_int
+        L.pa_acct_retire.argtypes = [AP, ctypes.c_int64]
+        L.pa_acct_retire.restype = ctypes.c_int
+        L.pa_pool_telemetry.argtypes = [AP, P, ctypes.c_int64, ctypes.POINTER(PoolTelemetry)]
+        L.pa_pool_telemetry.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -100,6 +144,8 @@ def library_path() -> str:
 def _check(fn: str, status: int) -> None:
     if status != PA_OK:
         msg = lib().pa_status_string(status).decode()
+        if status == PA_ERR_CAPACITY:
+            raise CapacityError(f"{fn}: {msg} (status {status})")
         if status in (PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE):
             raise ValueError(f"{fn}: {msg} (status {status})")
         raise PagedAttnError(fn, status, msg)
@@ -407,3 +453,107 @@ def prepare_decode_rope_append(q, k_new, v_new, k_cache, v_cache, block_tables, 
         return keep[5]
 
     return call
+
+
+# --- block pool ---
+
+def _int32_vec(t: torch.Tensor, name: str, n: int | None = None) -> None:
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or (n is not None and t.shape[0] != n):
+        raise ValueError(f"{name} must be contiguous int32 [{'' if n is None else n}]")
+
+
+def pool_init(free_ids: torch.Tensor, pool_state: torch.Tensor, num_free: int) -> None:
+    """Fresh pool: ids 0 .. num_free-1 on the stack free_ids (int32 [capacity]), pool_state int32 [8]."""
+    dev = _dev(free_ids, pool_state)
+    _int32_vec(free_ids, "free_ids")
+    _int32_vec(pool_state, "pool_state", 8)
+    with torch.cuda.device(dev):
+        st = lib().pa_pool_init(free_ids.data_ptr(), pool_state.data_ptr(), num_free, free_ids.shape[0], _stream(dev))
+    _check("pa_pool_init", st)
+
+
+def _assign_args(context_lens, query_start, block_tables, free_ids, pool_state, slot_mapping, block_size):
+    ts = [context_lens, block_tables, free_ids, pool_state, slot_mapping] + ([query_start] if query_start is not None else [])
+    dev = _dev(*ts)
+    _int32_vec(context_lens, "context_lens")
+    S = context_lens.shape[0]
+    if query_start is not None:
+        _int32_vec(query_start, "query_start", S + 1)
+    _int32_vec(free_ids, "free_ids")
+    _int32_vec(pool_state, "pool_state", 8)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [S, max_blocks]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1 or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be contiguous int64 [T]")
+    T = slot_mapping.shape[0]
+    args = (context_lens.data_ptr(), None if query_start is None else query_start.data_ptr(), block_tables.data_ptr(),
+            free_ids.data_ptr(), pool_state.data_ptr(), slot_mapping.data_ptr(), S, block_tables.shape[1],
+            block_size, T, free_ids.shape[0], _stream(dev))
+    return dev, args
+
+
+def assign_slots(context_lens: torch.Tensor, query_start, block_tables: torch.Tensor, free_ids: torch.Tensor,
+                 pool_state: torch.Tensor, slot_mapping: torch.Tensor, block_size: int) -> None:
+    """Blocks and slots for each sequence's new tokens (pa_assign_slots); query_start None: one token each."""
+    dev, args = _assign_args(context_lens, query_start, block_tables, free_ids, pool_state, slot_mapping, block_size)
+    with torch.cuda.device(dev):
+        st = lib().pa_assign_slots(*args)
+    _check("pa_assign_slots", st)
+
+
+def prepare_assign_slots(context_lens, query_start, block_tables, free_ids, pool_state, slot_mapping, block_size):
+    """A no-argument callable that repeats assign_slots with pre-marshalled arguments."""
+    dev, args = _assign_args(context_lens, query_start, block_tables, free_ids, pool_state, slot_mapping, block_size)
+    fn = lib().pa_assign_slots
+
+    def call():
+        st = fn(*args)
+        if st:
+            _check("pa_assign_slots", st)
+    return call
+
+
+def release_seqs(seq_ids: torch.Tensor, context_lens: torch.Tensor, block_tables: torch.Tensor,
+                 free_ids: torch.Tensor, pool_state: torch.Tensor, block_size: int) -> None:
+    """Push the listed sequences' blocks back on the stack (pa_release_seqs)."""
+    dev = _dev(seq_ids, context_lens, block_tables, free_ids, pool_state)
+    _int32_vec(seq_ids, "seq_ids")
+    _int32_vec(context_lens, "context_lens")
+    _int32_vec(free_ids, "free_ids")
+    _int32_vec(pool_state, "pool_state", 8)
+    S = context_lens.shape[0]
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S \
+            or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be contiguous int32 [S, max_blocks]")
+    with torch.cuda.device(dev):
+        st = lib().pa_release_seqs(seq_ids.data_ptr(), seq_ids.shape[0], context_lens.data_ptr(),
+                                   block_tables.data_ptr(), free_ids.data_ptr(), pool_state.data_ptr(), S,
+                                   block_tables.shape[1], block_size, free_ids.shape[0], _stream(dev))
+    _check("pa_release_seqs", st)
+
+
+def acct_init(num_blocks: int, block_size: int, bytes_per_block: int) -> PoolAcct:
+    a = PoolAcct()
+    _check("pa_acct_init", lib().pa_acct_init(ctypes.byref(a), num_blocks, block_size, bytes_per_block))
+    return a
+
+
+def acct_admit(acct: PoolAcct, max_tokens: int) -> None:
+    """Reserve for a request of at most max_tokens tokens; CapacityError if the pool cannot promise it."""
+    _check("pa_acct_admit", lib().pa_acct_admit(ctypes.byref(acct), max_tokens))
+
+
+def acct_retire(acct: PoolAcct, max_tokens: int) -> None:
+    _check("pa_acct_retire", lib().pa_acct_retire(ctypes.byref(acct), max_tokens))
+
+
+def pool_telemetry(acct: PoolAcct, state_host, tokens_stored: int) -> dict:
+    """Occupancy and bytes from the accounting and a host copy of pool_state (8 int32)."""
+    st = torch.as_tensor(state_host, dtype=torch.int32).contiguous().cpu()
+    if st.shape != (8,):
+        raise ValueError("state_host must hold the 8 int32 of pool_state")
+    out = PoolTelemetry()
+    _check("pa_pool_telemetry", lib().pa_pool_telemetry(ctypes.byref(acct), ctypes.c_void_p(st.data_ptr()),
+                                                        tokens_stored, ctypes.byref(out)))
+    return out.as_dict()

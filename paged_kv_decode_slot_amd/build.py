@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "pagedattn.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("pagedattn.hip", "blockpool.hip")]
 HEADER = os.path.join(ROOT, "include", "pagedattn.h")
 LIB = os.path.join(PKG, "libpagedattn.so")
 
@@ -30,7 +30,7 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

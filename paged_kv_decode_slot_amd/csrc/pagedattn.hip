@@ -1636,6 +1636,8 @@ const char* pa_status_string(pa_status_t status) {
             return "workspace missing or too small";
         case PA_ERR_HIP:
             return "HIP runtime error";
+        case PA_ERR_CAPACITY:
+            return "block pool capacity exceeded";
     }
     return "unknown status";
 }

@@ -35,9 +35,9 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = pa.lib()
-    assert L.pa_abi_version() == 1
-    for st in range(5):
-        assert L.pa_status_string(st)
+    assert L.pa_abi_version() == 2
+    for st in range(6):
+        assert L.pa_status_string(st) != b"unknown status"
     assert L.pa_status_string(99) == b"unknown status"
 
 
@@ -192,3 +192,76 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         pa.write_kv(torch.zeros(1, 2, 64, dtype=torch.bfloat16), torch.zeros(1, 2, 64, dtype=torch.bfloat16),
                     torch.zeros(1, dtype=torch.int64), k, v)
+
+
+# --- block pool: argument checks (no launch) and the host-side accounting ---
+
+def test_pool_calls_reject_bad_arguments():
+    L = pa.lib()
+    assert L.pa_pool_init(A, A, 5, 4, None) == pa.binding.PA_ERR_INVALID_ARG  # more free than capacity
+    assert L.pa_pool_init(A, A + 4, 2, 4, None) == pa.binding.PA_ERR_INVALID_ARG  # state not 8-byte aligned
+    assert L.pa_pool_init(A, None, 2, 4, None) == pa.binding.PA_ERR_INVALID_ARG
+    assert L.pa_pool_init(None, A, 0, 4, None) == pa.binding.PA_ERR_INVALID_ARG
+
+    def assign(ctx=A, qs=A, bt=A, free=A, state=A, slots=A, S=2, M=4, B=16, T=3, cap=8):
+        return L.pa_assign_slots(ctx, qs, bt, free, state, slots, S, M, B, T, cap, None)
+    bad = pa.binding.PA_ERR_INVALID_ARG
+    assert assign(S=-1) == bad
+    assert assign(qs=None, T=3) == bad       # one row per sequence needs T == S
+    assert assign(M=0) == bad
+    assert assign(B=0) == bad
+    assert assign(M=1 << 28, B=32) == bad    # a row would address more than 2^31 positions
+    assert assign(ctx=None) == bad
+    assert assign(bt=None) == bad
+    assert assign(state=A + 4) == bad
+    assert assign(slots=A + 4) == bad
+    assert assign(cap=-1) == bad
+    assert assign(S=0, T=1) == bad
+    assert assign(S=0, T=0) == pa.binding.PA_OK  # nothing to do: no launch
+
+    def release(ids=A, R=2, ctx=A, bt=A, free=A, state=A, S=2, M=4, B=16, cap=8):
+        return L.pa_release_seqs(ids, R, ctx, bt, free, state, S, M, B, cap, None)
+    assert release(R=-1) == bad
+    assert release(ids=None) == bad
+    assert release(state=A + 4) == bad
+    assert release(B=0) == bad
+    assert release(R=0, ids=None) == pa.binding.PA_OK  # nothing to release: no launch
+
+
+def test_admission_reserves_the_worst_case():
+    # B = 16, 10 blocks.  Reservations are ceil(max_tokens / 16): 33 -> 3 blocks,
+    # 160 -> 10 (refused beside the 3), 112 -> 7 (exactly fills), 1 -> 1 (refused).
+    a = pa.acct_init(10, 16, 4096)
+    pa.acct_admit(a, 33)
+    with pytest.raises(pa.CapacityError):
+        pa.acct_admit(a, 160)
+    assert a.reserved_blocks == 3 and a.refused == 1 and a.admitted == 1
+    pa.acct_admit(a, 112)
+    assert a.reserved_blocks == 10 and a.peak_reserved_blocks == 10
+    with pytest.raises(pa.CapacityError):
+        pa.acct_admit(a, 1)
+    pa.acct_admit(a, 0)  # a request that can never hold a token reserves nothing
+    pa.acct_retire(a, 0)
+    pa.acct_retire(a, 33)
+    assert a.reserved_blocks == 7 and a.admitted == 1 and a.peak_reserved_blocks == 10
+    pa.acct_admit(a, 48)
+    assert a.reserved_blocks == 10
+    with pytest.raises(ValueError):
+        pa.acct_retire(a, 1000)  # more than is reserved
+    with pytest.raises(ValueError):
+        pa.acct_admit(a, -1)
+
+
+def test_telemetry_from_the_state_record():
+    bpb = 2 * 8 * 16 * 128 * 2  # K and V of one block: Hkv 8, B 16, D 128, bf16
+    a = pa.acct_init(10, 16, bpb)
+    pa.acct_admit(a, 100)
+    # 4 free, 2 sequences refused, lowest top 1, 1 release refused
+    t = pa.pool_telemetry(a, [4, 2, 1, 1, 0, 0, 0, 0], tokens_stored=80)
+    assert t["used_blocks"] == 6 and t["free_blocks"] == 4 and t["peak_used_blocks"] == 9
+    assert t["used_bytes"] == 6 * bpb and t["capacity_bytes"] == 10 * bpb
+    assert t["empty_slots"] == 6 * 16 - 80 and t["occupancy"] == pytest.approx(0.6)
+    assert t["reserved_blocks"] == 7 and t["admitted"] == 1
+    assert (t["refused_sequences"], t["refused_releases"], t["refused_admissions"]) == (2, 1, 0)
+    with pytest.raises(ValueError):
+        pa.pool_telemetry(a, [4, 0, 4, 0, 0, 0, 0, 0], tokens_stored=97)  # more tokens than used slots
