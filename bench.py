@@ -241,6 +241,58 @@ def measure_rope(n, theta, args, device):
                 two_calls_note="copies of q and k_new (pa_rope works in place), pa_rope, pa_decode_append")
 
 
+def measure_pool(n, args, device):
+    """The block pool on workload n: the whole batch admitted by one
+    pa_assign_slots call (its context lengths as the prompts), timed over fresh
+    pools; then K decode steps, every sequence growing by one token per step on
+    the pool as the earlier steps left it, back to back."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+    from paged_kv_decode_slot_amd import workloads as W
+
+    case = W.config_case(n)
+    S, B = case.S, case.B
+    K, warm = args.steps, args.warmup
+    grow = -(-(K + warm) // B) + 1
+    M = case.block_tables.shape[1] + grow
+    cap = case.num_blocks + S * grow
+    i32 = dict(dtype=torch.int32, device=device)
+    free = torch.empty(cap, **i32)
+    state = torch.empty(8, **i32)
+    bt = torch.empty((S, M), **i32)
+    L0 = case.context_lens.astype(np.int32)
+    qs0 = np.concatenate([[0], np.cumsum(L0)]).astype(np.int32)
+    T0 = int(qs0[-1])
+    ctx0, qs0_d = torch.from_numpy(L0).to(device), torch.from_numpy(qs0).to(device)
+    slots0 = torch.empty(T0, dtype=torch.int64, device=device)
+    admit = pa.prepare_assign_slots(ctx0, qs0_d, bt, free, state, slots0, B)
+
+    def reset():
+        bt.fill_(-1)
+        pa.pool_init(free, state, cap)
+    reps = 20
+    admit_us = time_each([[reset, admit]], reps, 3)[1]
+    reset()
+    admit()
+    lens = [torch.from_numpy((L0 + k + 1).astype(np.int32)).to(device) for k in range(warm + K)]
+    slots = torch.empty(S, dtype=torch.int64, device=device)
+    steps = [pa.prepare_assign_slots(lens[k], None, bt, free, state, slots, B) for k in range(warm + K)]
+    for k in range(warm):
+        steps[k]()
+    torch.cuda.synchronize()
+    ms = time_back_to_back(steps[warm:], K, 0)
+    st = state.cpu().numpy()
+    assert st[1] == 0, "the pool refused a sequence"
+    a_mean = float(np.mean(admit_us))
+    return dict(workload=W.CONFIGS[n]["name"], admit_tokens=T0, admit_us_mean=round(a_mean, 2), admit_us_p50=round(pct(admit_us, 50), 2),
+                admit_slots_per_s=round(T0 / (a_mean * 1e-6)),
+                decode_step_us=round(ms * 1e3 / K, 2), decode_steps=K, seqs=S,
+                pool_blocks=cap, blocks_used_after=int(cap - st[0]),
+                note="launch-bound: the decode step reads lengths and writes one int64 slot per sequence")
+
+
 # Measured HBM traffic of the decode kernel (two rocprofv3 counter passes, scaled by a
 # plain copy of known size), kept with the hash of the source it was measured on.
 TRAFFIC_FILES = {(3, "fused"): "profiles/decode_append_kernel_C3_llama3-8b_bf16_counters.txt",
@@ -305,6 +357,7 @@ def main():
                     help="also time pa_attend with this many query tokens per sequence (0: skip)")
     ap.add_argument("--rope-theta", type=float, default=500000.0,
                     help="also time the step with the rotary embedding fused in, at this base (0: skip)")
+    ap.add_argument("--no-pool", action="store_true", help="skip the block-pool leg")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -360,6 +413,11 @@ def main():
     rope = None
     if args.rope_theta > 0:
         rope = measure_rope(args.config, args.rope_theta, args, device)
+        torch.cuda.empty_cache()
+
+    pool = None
+    if not args.no_pool:
+        pool = measure_pool(args.config, args, device)
         torch.cuda.empty_cache()
 
     cpu = None
@@ -420,6 +478,7 @@ def main():
             },
             "attend": attend,
             "rope": rope,
+            "pool": pool,
             "other": other,
         },
     }

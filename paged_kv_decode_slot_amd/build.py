@@ -28,18 +28,36 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, *SRCS]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _run(cmds, verbose):
+    """Run the commands in parallel; raise with the compiler's messages if one fails."""
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    failed = []
+    for p in procs:
+        out, _ = p.communicate()
+        msgs = [ln for ln in out.splitlines() if noise not in ln and ln.strip()]
+        if p.returncode != 0:
+            failed.append("\n".join(msgs))
+        elif verbose and msgs:
+            print("\n".join(msgs))
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+
+
+def build(verbose: bool = False) -> str:
+    """Compile each source to an object (in parallel), then link the shared library."""
+    objs = [LIB + "." + os.path.splitext(os.path.basename(src))[0] + ".o" for src in SRCS]
+    inc = ["-I", os.path.join(ROOT, "include")]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    _run([[HIPCC, *compile_flags, *inc, "-c", "-o", obj, src] for src, obj in zip(SRCS, objs)], verbose)
+    tmp = LIB + ".tmp"
+    _run([[HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]], verbose)
+    for obj in objs:
+        os.remove(obj)
     os.replace(tmp, LIB)
     return LIB
 

@@ -26,8 +26,8 @@
 namespace {
 
 constexpr int kPoolThreads = 256;      // one sequence (or release entry) per thread of a workgroup
-constexpr int kRowsPerGroup = 4096;    // token rows one workgroup fills before the rows are split further
-constexpr int kMaxRowSplit = 256;
+constexpr int kRowsPerGroup = 1024;    // token rows one workgroup fills before the rows are split further
+constexpr int kMaxRowSplit = 1024;
 
 // Fields of the state record (int32[8]); [4..5] hold a 64-bit arrival word:
 // (workgroups arrived << 32) | blocks popped, zero between calls.
@@ -86,9 +86,13 @@ __device__ inline int64_t group_inclusive_scan(int64_t v, int64_t* buf) {
 // The last workgroup to arrive gets true.  `popped` is this workgroup's share
 // of the blocks taken; the caller of a true result gets the call's total.
 __device__ inline bool arrive_last(int32_t* state, uint32_t popped, uint32_t* total_popped) {
+    const uint32_t groups = gridDim.x * gridDim.y;
+    if (groups == 1) {  // alone: no count to keep
+        *total_popped = popped;
+        return true;
+    }
     auto* word = reinterpret_cast<unsigned long long*>(state + kArrive);
     const unsigned long long old = atomicAdd(word, (1ull << 32) | popped);
-    const uint32_t groups = gridDim.x * gridDim.y;
     *total_popped = (uint32_t)old + popped;
     return (uint32_t)(old >> 32) == groups - 1;
 }
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(kPoolThreads) void assign_kernel(AssignArgs a) {
             const int32_t new_top = (int32_t)(top0 - total);
             a.state[kTop] = new_top;
             if (new_top < a.state[kLowWater]) a.state[kLowWater] = new_top;
-            *reinterpret_cast<unsigned long long*>(a.state + kArrive) = 0ull;
+            if (gridDim.x * gridDim.y > 1) *reinterpret_cast<unsigned long long*>(a.state + kArrive) = 0ull;
         }
     }
 }
@@ -251,7 +255,7 @@ __global__ __launch_bounds__(kPoolThreads) void release_kernel(ReleaseArgs a) {
         if (arrive_last(a.state, 0, &unused)) {
             if (ok) a.state[kTop] = (int32_t)(top0 + total);
             else a.state[kRefusedReleases] += 1;
-            *reinterpret_cast<unsigned long long*>(a.state + kArrive) = 0ull;
+            if (gridDim.x > 1) *reinterpret_cast<unsigned long long*>(a.state + kArrive) = 0ull;
         }
     }
 }
