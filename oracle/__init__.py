@@ -54,6 +54,8 @@ def _load():
         lib.oracle_round.restype = I
         lib.oracle_widen.argtypes = [P, I64, I, P]
         lib.oracle_widen.restype = None
+        lib.oracle_rmsnorm.argtypes = [P, P, P, P, P, I64, I, I, ctypes.c_double]
+        lib.oracle_rmsnorm.restype = I
         lib.oracle_pool_init.argtypes = [P, P, I]
         lib.oracle_pool_init.restype = None
         lib.oracle_assign_slots.argtypes = [P, P, P, P, P, P, I, I, I]
@@ -244,3 +246,23 @@ def release_seqs(seq_ids, context_lens: np.ndarray, block_tables: np.ndarray, fr
                                      _ptr(state), S, block_tables.shape[1], B, free_ids.shape[0])
     if rc:
         raise ValueError("oracle_release_seqs: bad argument")
+
+
+# --- RMSNorm ---
+
+def rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, residual: torch.Tensor | None = None):
+    """float64 RMSNorm of the rows of x ([T, H], storage dtype) with weight [H]:
+    returns y [T, H] before rounding, or (y, new_residual) when residual is given
+    (new_residual = x + residual rounded to the dtype, the row that is normalised)."""
+    T, H = x.shape
+    assert weight.shape == (H,) and weight.dtype == x.dtype
+    out = np.empty((T, H), dtype=np.float64)
+    res = np.empty((T, H), dtype=np.float64) if residual is not None else None
+    if residual is not None:
+        assert residual.shape == x.shape and residual.dtype == x.dtype
+    rc = _load().oracle_rmsnorm(_ptr(x.contiguous()), None if residual is None else _ptr(residual.contiguous()),
+                                _ptr(weight.contiguous()), _ptr(out), None if res is None else _ptr(res), T, H,
+                                _DTYPE_CODE[x.dtype], float(np.float32(eps)))
+    if rc:
+        raise ValueError("oracle_rmsnorm: bad argument")
+    return out if residual is None else (out, res)

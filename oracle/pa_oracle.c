@@ -525,3 +525,37 @@ int oracle_release_seqs(const int32_t* ids, int R, const int32_t* ctx, int32_t* 
     }
     return 0;
 }
+
+/*
+ * RMSNorm (ForgeLLM README, feature list: RMSNorm in the Llama-family decoder,
+ * with a reference, a fused and a compiled kernel checked against each
+ * other).  For each row x of H values and the weight w:
+ *   ms = (1/H) * sum_d x_d^2,   y_d = x_d * w_d / sqrt(ms + eps)
+ * in double, sums in index order; out holds y before any rounding.  With a
+ * residual (the fused form a decoder uses between sublayers), the row first
+ * becomes h = round_to_dtype(x + residual), which is stored back as the new
+ * residual (res_out, doubles the dtype holds exactly), and h is normalised.
+ * x, residual: [T][H], w: [H], all in the storage dtype; eps is the float
+ * value the caller passes, widened exactly.
+ */
+int oracle_rmsnorm(const void* x, const void* residual, const void* w, double* out, double* res_out, int64_t T,
+                   int H, int dtype, double eps) {
+    if (H <= 0 || T < 0 || eps < 0) return -1;
+    double* h = (double*)malloc(sizeof(double) * (size_t)H);
+    if (!h) return -2;
+    for (int64_t t = 0; t < T; ++t) {
+        const size_t row = (size_t)t * H;
+        for (int d = 0; d < H; ++d) h[d] = widen(x, row + d, dtype);
+        if (residual) {
+            for (int d = 0; d < H; ++d) h[d] += widen(residual, row + d, dtype);
+            oracle_round(h, H, dtype, h);
+            for (int d = 0; d < H; ++d) res_out[row + d] = h[d];
+        }
+        double ss = 0.0;
+        for (int d = 0; d < H; ++d) ss += h[d] * h[d];
+        const double r = 1.0 / sqrt(ss / H + eps);
+        for (int d = 0; d < H; ++d) out[row + d] = h[d] * widen(w, (size_t)d, dtype) * r;
+    }
+    free(h);
+    return 0;
+}
