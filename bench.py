@@ -293,6 +293,38 @@ def measure_pool(n, args, device):
                 note="launch-bound: the decode step reads lengths and writes one int64 slot per sequence")
 
 
+def measure_norm(args, device):
+    """pa_rmsnorm on Llama-3-8B rows (hidden 4096, bf16, eps 1e-5): a prefill
+    chunk of 16384 rows (HBM-bound; buffers rotated so the 256 MB MALL holds
+    none of a step's inputs) plain and fused with the residual add, and a
+    decode batch of 64 rows, K launches back to back each."""
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+
+    H, dt = 4096, torch.bfloat16
+    g = torch.Generator(device=device).manual_seed(0)
+    w = torch.randn(H, device=device, generator=g).to(dt)
+    res = {}
+    for rows in (16384, 64):
+        sets = 4 if rows > 1024 else 1
+        xs = [torch.randn((rows, H), device=device, generator=g).to(dt) for _ in range(sets)]
+        rs = [torch.randn((rows, H), device=device, generator=g).to(dt) for _ in range(sets)]
+        outs = [torch.empty_like(xs[0]) for _ in range(sets)]
+        plain = [pa.prepare_rmsnorm(xs[i], w, 1e-5, outs[i]) for i in range(sets)]
+        fused = [pa.prepare_rmsnorm(xs[i], w, 1e-5, outs[i], residual=rs[i]) for i in range(sets)]
+        row_bytes = H * 2
+        for name, calls, nbytes in (("plain", plain, 2 * rows * row_bytes + row_bytes),
+                                    ("fused_residual", fused, 4 * rows * row_bytes + row_bytes)):
+            ms = time_back_to_back(calls, args.steps, args.warmup)
+            us = ms * 1e3 / args.steps
+            res[f"{name}_{rows}"] = dict(us=round(us, 2), bytes=nbytes, gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                                         frac_of_peak=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+        del xs, rs, outs
+    return dict(workload="RMSNorm, Llama-3-8B rows: hidden 4096, bf16, eps 1e-5; 16384 rows (prefill chunk), 64 rows (decode batch)",
+                **res)
+
+
 # Measured HBM traffic of the decode kernel (two rocprofv3 counter passes, scaled by a
 # plain copy of known size), kept with the hash of the source it was measured on.
 TRAFFIC_FILES = {(3, "fused"): "profiles/decode_append_kernel_C3_llama3-8b_bf16_counters.txt",
@@ -358,6 +390,7 @@ def main():
     ap.add_argument("--rope-theta", type=float, default=500000.0,
                     help="also time the step with the rotary embedding fused in, at this base (0: skip)")
     ap.add_argument("--no-pool", action="store_true", help="skip the block-pool leg")
+    ap.add_argument("--no-norm", action="store_true", help="skip the RMSNorm leg")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -413,6 +446,11 @@ def main():
     rope = None
     if args.rope_theta > 0:
         rope = measure_rope(args.config, args.rope_theta, args, device)
+        torch.cuda.empty_cache()
+
+    norm = None
+    if not args.no_norm:
+        norm = measure_norm(args, device)
         torch.cuda.empty_cache()
 
     pool = None
@@ -479,6 +517,7 @@ def main():
             "attend": attend,
             "rope": rope,
             "pool": pool,
+            "rmsnorm": norm,
             "other": other,
         },
     }

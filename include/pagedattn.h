@@ -344,6 +344,23 @@ typedef struct pa_pool_telemetry {
 pa_status_t pa_pool_telemetry(const pa_pool_acct_t* acct, const int32_t* state_host, int64_t tokens_stored,
                               pa_pool_telemetry_t* out);
 
+/*
+ * RMSNorm of token rows (ForgeLLM README, feature list: RMSNorm in the
+ * Llama-family decoder, with reference, fused and compiled kernels checked
+ * against each other), optionally fused with the residual add before it:
+ *   h = x, or, when residual is not NULL, h = round(x + residual), which is
+ *       also stored back into residual;
+ *   out[t][d] = round(h[t][d] * weight[d] / sqrt(mean_d(h[t][d]^2) + eps))
+ * with float32 arithmetic and one rounding (nearest-even) into the dtype.
+ *   x, residual, out : [rows][hidden], weight : [hidden], one pa_dtype_t,
+ *       16-byte aligned, device; out may be x (each row is read before it is
+ *       written)
+ *   hidden : a multiple of 8 (16-bit) or 4 (f32), at most 8192 (16-bit) or
+ *       4096 (f32), else PA_ERR_UNSUPPORTED;  eps >= 0, finite
+ */
+pa_status_t pa_rmsnorm(const void* x, void* residual, const void* weight, void* out, int64_t rows, int32_t hidden,
+                       float eps, int32_t dtype, pa_stream_t stream);
+
 /* PA_ABI_VERSION of the built library. */
 int32_t pa_abi_version(void);
 

@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     pool_telemetry,
     prepare_assign_slots,
     release_seqs,
+    rmsnorm,
+    prepare_rmsnorm,
     attend,
     cache_desc,
     cache_shapes,

@@ -38,6 +38,7 @@ EXPORTS = (
     "pa_acct_admit",
     "pa_acct_retire",
     "pa_pool_telemetry",
+    "pa_rmsnorm",
     "pa_status_string",
     "pa_abi_version",
 )
@@ -118,6 +119,8 @@ def lib() -> ctypes.CDLL:
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_abi_version.argtypes = []
         L.pa_abi_version.restype = I32
+        L.pa_rmsnorm.argtypes = [P, P, P, P, ctypes.c_int64, I32, ctypes.c_float, I32, P]
+        L.pa_rmsnorm.restype = ctypes.c_int
         L.pa_pool_init.argtypes = [P, P, I32, I32, P]
         L.pa_pool_init.restype = ctypes.c_int
         L.pa_assign_slots.argtypes = [P, P, P, P, P, P, I32, I32, I32, I32, I32, P]
@@ -557,3 +560,46 @@ def pool_telemetry(acct: PoolAcct, state_host, tokens_stored: int) -> dict:
     _check("pa_pool_telemetry", lib().pa_pool_telemetry(ctypes.byref(acct), ctypes.c_void_p(st.data_ptr()),
                                                         tokens_stored, ctypes.byref(out)))
     return out.as_dict()
+
+
+# --- RMSNorm ---
+
+def _norm_args(x, weight, eps, out, residual):
+    ts = [x, weight, out] + ([residual] if residual is not None else [])
+    dev = _dev(*ts)
+    if x.dim() != 2 or weight.shape != (x.shape[1],) or out.shape != x.shape:
+        raise ValueError("x and out must be [rows, hidden], weight [hidden]")
+    if residual is not None and residual.shape != x.shape:
+        raise ValueError("residual must be [rows, hidden]")
+    if x.dtype not in _DTYPE_CODE or any(t.dtype != x.dtype for t in ts):
+        raise ValueError("tensors must share one of float32/float16/bfloat16")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("tensors must be contiguous")
+    args = (x.data_ptr(), None if residual is None else residual.data_ptr(), weight.data_ptr(), out.data_ptr(),
+            x.shape[0], x.shape[1], ctypes.c_float(eps), _DTYPE_CODE[x.dtype], _stream(dev))
+    return dev, args
+
+
+def rmsnorm(x: torch.Tensor, weight: torch.Tensor, eps: float, out: torch.Tensor | None = None,
+            residual: torch.Tensor | None = None) -> torch.Tensor:
+    """RMSNorm of the rows of x (pa_rmsnorm).  With residual, residual <- round(x + residual)
+    in place and that row is normalised.  out may be x."""
+    if out is None:
+        out = torch.empty_like(x)
+    dev, args = _norm_args(x, weight, eps, out, residual)
+    with torch.cuda.device(dev):
+        st = lib().pa_rmsnorm(*args)
+    _check("pa_rmsnorm", st)
+    return out
+
+
+def prepare_rmsnorm(x, weight, eps, out, residual=None):
+    """A no-argument callable that repeats rmsnorm with pre-marshalled arguments."""
+    dev, args = _norm_args(x, weight, eps, out, residual)
+    fn = lib().pa_rmsnorm
+
+    def call():
+        st = fn(*args)
+        if st:
+            _check("pa_rmsnorm", st)
+    return call

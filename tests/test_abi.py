@@ -265,3 +265,24 @@ def test_telemetry_from_the_state_record():
     assert (t["refused_sequences"], t["refused_releases"], t["refused_admissions"]) == (2, 1, 0)
     with pytest.raises(ValueError):
         pa.pool_telemetry(a, [4, 0, 4, 0, 0, 0, 0, 0], tokens_stored=97)  # more tokens than used slots
+
+
+def test_rmsnorm_rejects_bad_arguments():
+    L = pa.lib()
+    bad, uns = pa.binding.PA_ERR_INVALID_ARG, pa.binding.PA_ERR_UNSUPPORTED
+
+    def norm(x=A, res=None, w=A, out=A, rows=4, H=4096, eps=1e-5, dt=2):
+        return L.pa_rmsnorm(x, res, w, out, rows, H, ctypes.c_float(eps), dt, None)
+    assert norm(rows=-1) == bad
+    assert norm(H=0) == bad
+    assert norm(eps=-1.0) == bad
+    assert norm(eps=float("nan")) == bad
+    assert norm(eps=float("inf")) == bad
+    assert norm(dt=7) == bad
+    assert norm(H=12) == uns            # not whole 16-byte pieces
+    assert norm(H=8200) == uns          # wider than 8192 (16-bit)
+    assert norm(H=4100, dt=0) == uns    # wider than 4096 (f32)
+    assert norm(x=None) == bad
+    assert norm(out=A + 8) == bad
+    assert norm(res=A + 4) == bad
+    assert norm(rows=0, x=None, w=None, out=None) == pa.binding.PA_OK  # nothing to do: no launch
