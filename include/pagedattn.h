@@ -134,12 +134,14 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 /*
  * pa_decode with the work split chosen by the caller:
  *   num_workers == 0  : automatic (what pa_decode does)
- *   num_workers == -1 : one wavefront per (sequence, kv-head) over its whole
- *                       context; no partial results, no merge
- *   num_workers  > 0  : the logical blocks of all (sequence, kv-head) pairs
- *                       are dealt to that many wavefronts in equal contiguous
- *                       runs; pairs cut between runs are merged by a
- *                       log-sum-exp reduction
+ *   num_workers == -1 : one worker per (sequence, kv-head slice) over its
+ *                       whole context; no partial results, no merge
+ *   num_workers  > 0  : the logical blocks of all sequences are dealt to that
+ *                       many workers in equal contiguous runs; pairs cut
+ *                       between runs are merged by a log-sum-exp reduction
+ * A worker is one workgroup with a wavefront per kv-head of a slice of the
+ * kv-heads (the slice is the largest divisor of num_kv_heads up to 2), so
+ * every wave of a worker covers the same logical blocks.
  * Every choice computes the same function; results agree within rounding.
  */
 pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,

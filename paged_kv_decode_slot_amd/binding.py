@@ -264,7 +264,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
            num_workers: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Decode attention of q [S, Hq, D] over the paged caches; returns out [S, Hq, D].
 
-    num_workers: 0 automatic, -1 one wavefront per (sequence, kv-head), >0 that many.
+    num_workers: 0 automatic, -1 one worker per (sequence, kv-head slice), >0 that many
+    workers (a worker is a workgroup with one wavefront per kv-head of a slice).
     workspace: optional uint8 device tensor; one is allocated when not given.
     """
     dev, out, args, _keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,

@@ -10,16 +10,22 @@
 // HBM exactly once, with 16-byte coalesced loads, and the arithmetic runs on
 // the matrix cores so that it stays off the critical path.
 //
-// Design (one wavefront = one worker):
-//  * Work unit = one (sequence, kv-head, logical block).  All units of the
-//    batch are laid end to end, sequence-major then kv-head then block, and
-//    dealt to the workers in equal contiguous runs ("stream-K"), so every
-//    worker streams the same number of blocks whatever the length mix.  A
-//    run that covers a whole (sequence, kv-head) writes the output directly;
-//    one that covers part of it stores (o, log-sum-exp), and the wave that
-//    stores the last part of a pair merges the parts, inside the same launch.
-//    The split depends only on the lengths and the worker count, so results
-//    are bitwise reproducible and independent of physical placement.
+// Design (one workgroup = one worker, one wavefront per kv-head of a slice):
+//  * The kv-heads are taken in slices of up to 2 (the largest divisor of
+//    their count that fits).  Work unit = one (sequence, slice, logical
+//    block).  All units of the batch are laid end to end, sequence-major then
+//    slice then block, and dealt to the workers in equal contiguous runs
+//    ("stream-K"), so every worker streams the same number of blocks whatever
+//    the length mix.  Wave i of a worker takes kv-head i of the slice over the
+//    worker's blocks: the waves of a workgroup read the neighbouring tiles of
+//    the same physical block together (one block's kv-heads are contiguous in
+//    the pool), and a split of a sequence is shared by all of its heads
+//    instead of multiplying the partial results.  A run that covers a whole
+//    (sequence, kv-head) writes the output directly; one that covers part of
+//    it stores (o, log-sum-exp), and the wave that stores the last part of a
+//    pair merges the parts, inside the same launch.  The split depends only
+//    on the lengths and the worker count, so results are bitwise
+//    reproducible and independent of physical placement.
 //  * Per 16-token tile, the G query heads of a kv-head form the columns of
 //    one 16x16 MFMA tile: S = K * Q^T (tokens x heads), then O^T += V^T * P^T
 //    (dims x heads).  P comes out of the first product in exactly the lane
@@ -42,18 +48,18 @@
 namespace {
 
 constexpr int kWave = 64;
-#ifndef PA_WAVES_PER_GROUP
-#define PA_WAVES_PER_GROUP 2
+#ifndef PA_MAX_SLICE
+#define PA_MAX_SLICE 2
 #endif
-constexpr int kWavesPerGroup = PA_WAVES_PER_GROUP;
-constexpr int kGroupThreads = kWave * kWavesPerGroup;
+constexpr int kMaxSlice = PA_MAX_SLICE;            // kv-heads (waves) of one decode workgroup, at most
+constexpr int kGroupThreads = kWave * kMaxSlice;  // the largest decode workgroup
 constexpr int kWriteThreads = 256;
 constexpr int kMaxSeqs = 4096;
 constexpr int kMaxGroup = 16;
-#ifndef PA_WORKERS_PER_CU
-#define PA_WORKERS_PER_CU 2
+#ifndef PA_WAVES_PER_CU
+#define PA_WAVES_PER_CU 2
 #endif
-constexpr int kWorkersPerCU = PA_WORKERS_PER_CU;
+constexpr int kWavesPerCU = PA_WAVES_PER_CU;  // automatic split: decode waves per compute unit
 constexpr int kMinBlocksPerWorker = 16;
 constexpr int kMaxWorkers = 1 << 20;
 constexpr int kMaxRopePairs = 64;  // head_dim / 2
@@ -212,8 +218,8 @@ struct DecodeArgs {
     const int32_t* context_lens;
     uint8_t* out;
     unsigned long long* arrivals;  // [num_seqs * Hkv]: (call tag << 32) | parts stored so far
-    float* part_lse;               // [workers][2][G]
-    float* part_o;                 // [workers][2][G][D]
+    float* part_lse;               // [workers * slice][2][cols]: per wave, two slots
+    float* part_o;                 // [workers * slice][2][cols][D]
     const uint8_t* k_new;          // append: [num_seqs][Hkv][D], the token at position ctx-1
     const uint8_t* v_new;
     uint8_t* k_cache_w;            // append: the same pools, written
@@ -226,10 +232,12 @@ struct DecodeArgs {
     int32_t group;
     int32_t max_blocks;
     int32_t num_blocks;
-    int32_t num_workers;
-    int32_t per_segment;  // 1: worker w owns (sequence, kv-head) w entirely
+    int32_t num_workers;  // attention workgroups
+    int32_t slice;        // kv-heads side by side in a worker: its waves
+    int32_t chunks;       // num_kv_heads / slice
+    int32_t per_segment;  // 1: worker w owns (sequence, slice) w entirely
     int32_t attn_groups;  // append: workgroups [attn_groups, grid) store the new rows
-    int32_t run_cost;     // extra units counted per (sequence, kv-head) with context (see load_lengths)
+    int32_t run_cost;     // extra units counted per (sequence, slice) with context (see load_lengths)
     int32_t cols;         // columns of a pair: G heads, or (several query tokens) tpc tokens x G heads
     const int32_t* query_start;  // several query tokens: [num_seqs + 1] query rows of each sequence
     int32_t chunk;        // several query tokens: this launch takes tokens [chunk*tpc, (chunk+1)*tpc) of each
@@ -263,9 +271,10 @@ __device__ inline int clamp_ctx(int ctx, int B, int max_blocks) {
 
 // Context lengths (clamped) and the exclusive prefix over sequences of their
 // unit counts, into LDS: ctx[S], pre[S + 1].  A sequence with nb > 0 blocks
-// counts nb + run_cost units per kv-head: the work split deals out units, and
-// the first run_cost units of a pair stand for the cost of starting a run on
-// it (loading Q, waiting for the first tile) and hold no blocks.
+// counts nb + run_cost units per slice of kv-heads: the work split deals out
+// units, and the first run_cost units of a (sequence, slice) stand for the
+// cost of starting a run on it (loading Q, waiting for the first tile) and
+// hold no blocks.  Every wave of the workgroup takes part.
 //
 // With several query tokens per sequence (MQ), this launch's pair of sequence
 // s holds its query tokens i in [i0, i0 + rows), i0 = chunk * tpc; they see
@@ -276,8 +285,8 @@ template <int B, bool MQ>
 __device__ __attribute__((always_inline)) void load_lengths(const DecodeArgs& a, int32_t* ctx, int32_t* pre, int32_t* row0, int32_t* rows,
                              int32_t* wave_tot) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int S = a.num_seqs;
-    const int per = (S + kGroupThreads - 1) / kGroupThreads;
+    const int S = a.num_seqs, nthreads = blockDim.x;
+    const int per = (S + nthreads - 1) / nthreads;
     const int lo = min(S, tid * per), hi = min(S, lo + per);
     int sum = 0;
     for (int i = lo; i < hi; ++i) {
@@ -307,7 +316,7 @@ __device__ __attribute__((always_inline)) void load_lengths(const DecodeArgs& a,
         pre[i] = run;
         run += ctx[i] > 0 ? (ctx[i] + B - 1) / B + a.run_cost : 0;
     }
-    if (tid == kGroupThreads - 1) pre[S] = run;
+    if (tid == nthreads - 1) pre[S] = run;
     __syncthreads();
 }
 
@@ -572,8 +581,10 @@ struct Tile {
     uint4 v[Cfg<DT, D, B>::kVPiece];
 };
 
-// Where a worker's partial result for one split (sequence, kv-head) lives.
-__device__ inline size_t part_index(int64_t w, int slot, int G, int h) { return ((size_t)w * 2 + slot) * G + h; }
+// Where a wave's partial result for one split (sequence, kv-head) lives: wave
+// wid = worker * slice + (kv-head within the slice), slot 0 for the worker's
+// first run and 1 for its last.
+__device__ inline size_t part_index(int64_t wid, int slot, int G, int h) { return ((size_t)wid * 2 + slot) * G + h; }
 
 // Reductions over the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48:
 // one head's four row groups).  permlane16/32_swap leave, in the two halves of
@@ -658,20 +669,25 @@ __device__ inline float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_offset
 // keeps their float4 accumulators in registers.  Parts are taken 64 at a
 // time: the lanes read one part's NC log-sum-exps each, and per column the
 // wave forms the running maximum M, the weights 2^(lse - M) and their sum.
-// The outputs are read PB = 16/UPL parts per batch, 16 16-byte loads in
-// flight per lane; the first batch is issued before the log-sum-exps, so a
-// merge of up to PB parts costs one round trip to memory.  Only the first
+// The outputs are read PB = kMergeLoads/UPL parts per batch, kMergeLoads
+// 16-byte loads in flight per lane; the first batch is issued before the
+// log-sum-exps, so a merge of up to PB parts costs one round trip to memory.  Only the first
 // `active` columns are stored (the rest pad the last token group).
+#ifndef PA_MERGE_LOADS
+#define PA_MERGE_LOADS 16
+#endif
+constexpr int kMergeLoads = PA_MERGE_LOADS;  // 16-byte loads per lane in one batch of a merge
+
 template <int DT, int D, int UPL, bool MQ>
 __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int parts,
-                           int64_t wa, int first_slot, bool unit_runs, int64_t U, int64_t W, int unit0,
-                           MergeLds& L) {
+                           int64_t wa, int first_slot, bool unit_runs, int64_t U, int64_t W, int hs, int wi,
+                           int unit0, MergeLds& L) {
     constexpr int E = DT == PA_F32 ? 4 : 2;
-    constexpr int PB = 16 / UPL;
+    constexpr int PB = kMergeLoads / UPL;
     const int lane = threadIdx.x & 63, NC = a.cols;
     const int NU = NC * D / 4;
     const int part_bytes = NC * D * 4;
-    const int lse_bytes = (int)(W * 2 * NC * 4);  // every worker's two slots of NC log-sum-exps
+    const int lse_bytes = (int)(W * hs * 2 * NC * 4);  // every wave's two slots of NC log-sum-exps
     const __amdgpu_buffer_rsrc_t lse_r =
         __builtin_amdgcn_make_buffer_rsrc(a.part_lse, (short)0, lse_bytes, kBufferWord3);
 
@@ -688,10 +704,11 @@ __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, i
     }
     __builtin_amdgcn_wave_barrier();
 
-    // Index of part k's first log-sum-exp (part_index(worker, slot, NC, 0)).
+    // Index of part k's first log-sum-exp (part_index(wave, slot, NC, 0)): the
+    // part's worker, and in it the wave of this pair's kv-head.
     auto part_loc = [&](int k) -> int64_t {
         const int64_t wk = unit_runs ? owner_of(F + k, U, W) : wa + k;
-        return (int64_t)part_index(wk, k == 0 ? first_slot : 0, NC, 0);
+        return (int64_t)part_index(wk * hs + wi, k == 0 ? first_slot : 0, NC, 0);
     };
     // Every slot of v is defined and read on every path (unused slots are zero
     // and weigh 0), so no load of the merge can be left pending where the
@@ -782,7 +799,7 @@ __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, i
 
 template <int DT, int D, bool MQ>
 __device__ __attribute__((always_inline)) void merge_parts(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int64_t Fv, int nb,
-                            int64_t U, int64_t W, MergeLds& L) {
+                            int64_t U, int64_t W, int hs, int wi, MergeLds& L) {
     const bool unit_runs = W >= U;
     const int64_t wa = owner_of(F, U, W);
     const int parts = unit_runs ? nb : (int)(owner_of(F + nb - 1, U, W) - wa + 1);
@@ -791,30 +808,31 @@ __device__ __attribute__((always_inline)) void merge_parts(const DecodeArgs& a, 
     const int first_slot = run_start(wa, U, W) >= Fv ? 0 : 1;
     const int units = a.cols * D / 4;  // 16-byte output units of the pair
     if (units <= kWave)
-        merge_body<DT, D, 1, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+        merge_body<DT, D, 1, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, hs, wi, 0, L);
     else if (units <= 2 * kWave)
-        merge_body<DT, D, 2, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+        merge_body<DT, D, 2, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, hs, wi, 0, L);
     else if (units <= 4 * kWave)
-        merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+        merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, hs, wi, 0, L);
     else if (MQ && units <= 8 * kWave)  // 16 columns of D = 128: one pass, 2 parts a batch
-        merge_body<DT, D, 8, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, 0, L);
+        merge_body<DT, D, 8, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, hs, wi, 0, L);
     else
         for (int u0 = 0; u0 < units; u0 += 4 * kWave)  // up to 256 units per pass
-            merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, u0, L);
+            merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, hs, wi, u0, L);
 }
 
 // Attend query group (s, kvh) over logical blocks [j0, j1) of sequence s, whose
-// pair (s, kvh) occupies units [F, F + nb).  A run over the whole context
-// writes out; otherwise the run stores a partial in slot `slot` of worker w,
-// and the wave that stores the pair's last partial merges them.  With several
+// (sequence, slice) occupies units [F, F + nb) of the split over W workers.
+// A run over the whole context writes out; otherwise the run stores a partial
+// in slot `slot` of wave wid (wave wi of its worker, which has hs waves), and
+// the wave that stores the pair's last partial merges them.  With several
 // query tokens (MODE kModeMulti) the pair's columns are its `rows` query
 // tokens (from query row row0) times the G heads, and column (i, h) sees
 // positions up to ctx - rows + i; otherwise the columns are the G heads of
 // sequence s's one token, which sees positions up to ctx - 1.
 template <int DT, int D, int B, int MODE>
 __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row0, int rows, int j0, int j1, int nb,
-                           int64_t F, int64_t Fv, int64_t U, int64_t W, int w, int slot, MergeLds& mlds,
-                           const double* rw) {
+                           int64_t F, int64_t Fv, int64_t U, int64_t W, int wid, int slot, int hs, int wi,
+                           MergeLds& mlds, const double* rw) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
     constexpr int NBUF = PA_TILE_BUFFERS;
@@ -1037,7 +1055,7 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
     {
         // The partial's outputs as 16-byte stores with the agent-coherence bit
         // (through a resource bounded to this part, so lanes past a.cols store nothing).
-        const size_t part0 = part_index(w, slot, a.cols, 0);
+        const size_t part0 = part_index(wid, slot, a.cols, 0);
         const __amdgpu_buffer_rsrc_t po = __builtin_amdgcn_make_buffer_rsrc(a.part_o + part0 * D, (short)0,
                                                                              a.cols * D * 4, kBufferWord3);
 #pragma unroll
@@ -1050,7 +1068,7 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
     const int parts = W >= U ? nb : (int)(owner_of(F + nb - 1, U, W) - owner_of(F, U, W) + 1);
     int last = 0;
     if (lane == 0) last = arrive(a.arrivals + (size_t)s * a.num_kv_heads + kvh, a.tag, parts) ? 1 : 0;
-    if (__shfl(last, 0)) merge_parts<DT, D, MQ>(a, s, kvh, row0, active, F, Fv, nb, U, W, mlds);
+    if (__shfl(last, 0)) merge_parts<DT, D, MQ>(a, s, kvh, row0, active, F, Fv, nb, U, W, hs, wi, mlds);
 }
 
 // Fused append, the store side: wave `wi` of the writer workgroups copies the
@@ -1151,20 +1169,30 @@ __device__ __attribute__((always_inline)) void store_new_rows(const DecodeArgs& 
     }
 }
 
-constexpr size_t kDecodeStaticLds = sizeof(MergeLds) * kWavesPerGroup + sizeof(int32_t) * kWavesPerGroup;
+// Static LDS of a decode workgroup: the per-wave totals of the length prefix
+// and the rotary frequencies.  The merge areas, one per wave, follow the
+// length arrays in the dynamic part (decode_len_words 32-bit words, a
+// multiple of 4 so that the areas start on a 16-byte boundary).
+constexpr size_t kDecodeStaticLds = sizeof(int32_t) * kMaxSlice + sizeof(double) * kMaxRopePairs;
+__host__ __device__ inline int decode_len_words(int num_seqs, bool multi) {
+    return (2 * num_seqs + 1 + (multi ? 2 * num_seqs : 0) + 3) & ~3;
+}
 
 #ifndef PA_MIN_WAVES_PER_SIMD
 #define PA_MIN_WAVES_PER_SIMD 1
 #endif
 
+// One launch: workgroups [0, num_workers) are the workers of the split, each
+// with `slice` waves; with the append fused in, the workgroups after them
+// store the new K/V rows.
 template <int DT, int D, int B, int MODE>
 __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
     using C = Cfg<DT, D, B>;
     constexpr bool APPEND = mode_appends(MODE), MQ = MODE == kModeMulti;
-    // ctx[num_seqs], pre[num_seqs + 1]; several query tokens: row0[num_seqs], rows[num_seqs]
-    extern __shared__ int32_t s_lds[];
-    __shared__ int32_t s_wave_tot[kWavesPerGroup];
-    __shared__ MergeLds s_merge[kWavesPerGroup];
+    // ctx[num_seqs], pre[num_seqs + 1]; several query tokens: row0[num_seqs], rows[num_seqs];
+    // then the merge areas.
+    extern __shared__ __attribute__((aligned(16))) int32_t s_lds[];
+    __shared__ int32_t s_wave_tot[kMaxSlice];
     // Rotary frequencies in LDS: lanes index them by their own dims, and a
     // lane-dependent index into the argument block would copy it to scratch.
     constexpr bool ROPE = MODE == kModeAppendRope;
@@ -1176,10 +1204,10 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         }
         __syncthreads();
     }
+    const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave in the workgroup
     if constexpr (APPEND) {
         if ((int)blockIdx.x >= a.attn_groups) {
-            store_new_rows<DT, D, B, ROPE>(a, (blockIdx.x - a.attn_groups) * kWavesPerGroup + (threadIdx.x >> 6),
-                                           s_rope_w);
+            store_new_rows<DT, D, B, ROPE>(a, (blockIdx.x - a.attn_groups) * (blockDim.x >> 6) + wi, s_rope_w);
             return;
         }
     }
@@ -1187,16 +1215,18 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
     int32_t* s_pre = s_lds + a.num_seqs;
     int32_t* s_row0 = s_pre + a.num_seqs + 1;
     int32_t* s_rows = s_row0 + a.num_seqs;
+    MergeLds* s_merge = reinterpret_cast<MergeLds*>(s_lds + decode_len_words(a.num_seqs, MQ));
     load_lengths<B, MQ>(a, s_ctx, s_pre, s_row0, s_rows, s_wave_tot);
 
     const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6));
-    if (w >= a.num_workers) return;
+    const int g = blockIdx.x;  // this worker
+    if (g >= a.num_workers) return;
     const int S = a.num_seqs, Hkv = a.num_kv_heads, G = a.group;
-    const int W = a.num_workers;
+    const int W = a.num_workers, hs = a.slice, hc = a.chunks;
+    const int wid = g * hs + wi;  // this wave among all workers' waves
 
-    // Query rows with no context get out = 0; worker w takes the pairs z = w (mod W).
-    for (int z = w; z < S * Hkv; z += W) {
+    // Query rows with no context get out = 0; wave wid takes the pairs z = wid (mod W * hs).
+    for (int z = wid; z < S * Hkv; z += W * hs) {
         const int s = z / Hkv, kvh = z % Hkv;
         if (s_ctx[s] != 0) continue;
         const int nrows = MQ ? s_rows[s] : 1;
@@ -1207,37 +1237,38 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         }
     }
 
-    const int64_t U = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[S]) * Hkv;  // uniform: a scalar loop
+    const int64_t U = (int64_t)__builtin_amdgcn_readfirstlane(s_pre[S]) * hc;  // uniform: a scalar loop
     int64_t start, end;
     if (a.per_segment) {
-        if (w >= S * Hkv) return;
-        const int s = w / Hkv, kvh = w % Hkv;
+        if (g >= S * hc) return;
+        const int s = g / hc, c = g % hc;
         const int nb = s_pre[s + 1] - s_pre[s];
-        start = (int64_t)s_pre[s] * Hkv + (int64_t)kvh * nb;
+        start = (int64_t)s_pre[s] * hc + (int64_t)c * nb;
         end = start + nb;
     } else {
-        start = (int64_t)w * U / W;
-        end = (int64_t)(w + 1) * U / W;
+        start = (int64_t)g * U / W;
+        end = (int64_t)(g + 1) * U / W;
     }
     for (int64_t u = start; u < end;) {
         // Every lane holds the same values; readfirstlane lets them live in scalar registers.
-        const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, (int)(u / Hkv)));
+        const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, (int)(u / hc)));
         const int base = __builtin_amdgcn_readfirstlane(s_pre[s]);
-        const int nbv = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - base;  // units of each pair
+        const int nbv = __builtin_amdgcn_readfirstlane(s_pre[s + 1]) - base;  // units of each slice
         const int ctx = __builtin_amdgcn_readfirstlane(s_ctx[s]);
         const int nb = (ctx + B - 1) / B;  // its blocks
         const int cost = nbv - nb;         // its leading units that hold no block
-        const int off = (int)(u - (int64_t)base * Hkv);
-        const int kvh = off / nbv, jv0 = off % nbv;
+        const int off = (int)(u - (int64_t)base * hc);
+        const int c = off / nbv, jv0 = off % nbv;
+        const int kvh = c * hs + wi;  // this wave's kv-head
         const int64_t left = end - u;
         const int jv1 = left < (int64_t)(nbv - jv0) ? jv0 + (int)left : nbv;
         const int j0 = jv0 > cost ? jv0 - cost : 0, j1 = jv1 - cost;
-        const int64_t Fv = (int64_t)base * Hkv + (int64_t)kvh * nbv;  // the pair's first unit
+        const int64_t Fv = (int64_t)base * hc + (int64_t)c * nbv;  // the (sequence, slice)'s first unit
         const int row0 = MQ ? __builtin_amdgcn_readfirstlane(s_row0[s]) : 0;
         const int rows = MQ ? __builtin_amdgcn_readfirstlane(s_rows[s]) : 1;
         if (j1 > j0)  // a range that ends inside the leading units holds no block
-            attend_run<DT, D, B, MODE>(a, s, kvh, ctx, row0, rows, j0, j1, nb, Fv + cost, Fv, U, W, w,
-                                       u == start ? 0 : 1, s_merge[threadIdx.x >> 6], s_rope_w);
+            attend_run<DT, D, B, MODE>(a, s, kvh, ctx, row0, rows, j0, j1, nb, Fv + cost, Fv, U, W, wid,
+                                       u == start ? 0 : 1, hs, wi, s_merge[wi], s_rope_w);
         u += jv1 - jv0;
     }
 }
@@ -1403,7 +1434,9 @@ pa_status_t check_cache(const pa_cache_desc_t* c) {
 }
 
 struct Plan {
-    int workers;
+    int workers;  // workgroups of the split
+    int slice;    // kv-heads per worker, one wave each
+    int chunks;   // num_kv_heads / slice
     int per_segment;
     size_t bytes;
     size_t off_lse;
@@ -1424,15 +1457,25 @@ pa_status_t check_decode_shapes(int32_t num_seqs, int32_t num_q_heads, int32_t m
     return PA_OK;
 }
 
+// Kv-heads a decode worker takes side by side (one wave each): the largest
+// divisor of their count that is at most kMaxSlice.
+int head_slice(int num_kv_heads) {
+    for (int h = kMaxSlice; h > 1; --h)
+        if (num_kv_heads % h == 0) return h;
+    return 1;
+}
+
 // Worker count and workspace layout; needs the device only for the automatic choice.
-// Workspace: arrival words [S * Hkv] (8 B each), then part_lse [W][2][cols], then
-// part_o [W][2][cols][D], where cols is a pair's column count (G, or tokens x G).
+// Workspace: arrival words [S * Hkv] (8 B each), then part_lse [W * slice][2][cols], then
+// part_o [W * slice][2][cols][D], where cols is a pair's column count (G, or tokens x G).
 pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, const pa_cache_desc_t* cache,
                       int32_t num_workers, int cols, Plan* plan) {
     const int Hkv = cache->num_kv_heads, G = cols, D = cache->head_dim;
-    *plan = Plan{0, 0, 0, 0, 0};
+    *plan = Plan{0, 1, 1, 0, 0, 0, 0};
+    plan->slice = head_slice(Hkv);
+    plan->chunks = Hkv / plan->slice;
     if (num_workers == -1) {
-        plan->workers = num_seqs * Hkv;
+        plan->workers = num_seqs * plan->chunks;
         plan->per_segment = 1;
         return PA_OK;
     }
@@ -1442,15 +1485,17 @@ pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
         int cus = 0;
         pa_status_t st = cu_count(&cus);
         if (st != PA_OK) return st;
-        const int64_t units_bound = (int64_t)num_seqs * Hkv * max_blocks;
+        const int64_t units_bound = (int64_t)num_seqs * plan->chunks * max_blocks;
         int64_t want = (units_bound + kMinBlocksPerWorker - 1) / kMinBlocksPerWorker;
-        const int64_t cap = (int64_t)cus * kWorkersPerCU;
+        const int64_t per_cu = kWavesPerCU / plan->slice;
+        const int64_t cap = (int64_t)cus * (per_cu < 1 ? 1 : per_cu);
         W = (int)(want < 1 ? 1 : (want > cap ? cap : want));
     }
     plan->workers = W;
+    const size_t waves = (size_t)W * plan->slice;
     const size_t arrivals = round_up(sizeof(unsigned long long) * (size_t)num_seqs * Hkv, 256);
-    const size_t lse = round_up(sizeof(float) * (size_t)W * 2 * G, 256);
-    const size_t o = sizeof(float) * (size_t)W * 2 * G * D;
+    const size_t lse = round_up(sizeof(float) * waves * 2 * G, 256);
+    const size_t o = sizeof(float) * waves * 2 * G * D;
     plan->off_lse = arrivals;
     plan->off_o = arrivals + lse;
     plan->bytes = arrivals + lse + o;
@@ -1467,16 +1512,17 @@ uint32_t next_tag() {
     return t;
 }
 
-// LDS bytes of one decode workgroup's per-sequence arrays (the dynamic part).
-size_t decode_dynamic_lds(int num_seqs, bool multi) {
-    return sizeof(int32_t) * (2 * (size_t)num_seqs + 1 + (multi ? 2 * (size_t)num_seqs : 0));
+// Dynamic LDS bytes of one decode workgroup: the per-sequence arrays and a
+// merge area per wave.
+size_t decode_dynamic_lds(int num_seqs, bool multi, int slice) {
+    return sizeof(int32_t) * (size_t)decode_len_words(num_seqs, multi) + sizeof(MergeLds) * (size_t)slice;
 }
 
 template <int DT, int D, int B, int MODE>
 hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stream) {
     using C = Cfg<DT, D, B>;
     constexpr bool APPEND = mode_appends(MODE);
-    const int groups = (plan.workers + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int groups = plan.workers;
     if (groups == 0) return hipSuccess;
     DecodeArgs args_copy = a;
     args_copy.attn_groups = groups;
@@ -1484,12 +1530,12 @@ hipError_t launch_decode(const DecodeArgs& a, const Plan& plan, hipStream_t stre
     if (APPEND) {
         constexpr int rows_per_wave = 64 / (D * C::kElt / 16);
         const int waves = (a.num_seqs * a.num_kv_heads + rows_per_wave - 1) / rows_per_wave;
-        writer_groups = (waves + kWavesPerGroup - 1) / kWavesPerGroup;
+        writer_groups = (waves + plan.slice - 1) / plan.slice;
     }
     void* args[] = {&args_copy};
-    const size_t lds = decode_dynamic_lds(a.num_seqs, MODE == kModeMulti);
+    const size_t lds = decode_dynamic_lds(a.num_seqs, MODE == kModeMulti, plan.slice);
     return hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, B, MODE>),
-                           dim3(groups + writer_groups), dim3(kGroupThreads), args, lds, stream);
+                           dim3(groups + writer_groups), dim3(kWave * plan.slice), args, lds, stream);
 }
 
 template <int DT, int MODE>
@@ -1577,6 +1623,8 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     a.max_blocks = max_blocks_per_seq;
     a.num_blocks = cache->num_blocks;
     a.num_workers = plan.workers;
+    a.slice = plan.slice;
+    a.chunks = plan.chunks;
     a.per_segment = plan.per_segment;
     a.cols = tpc * G;
     a.query_start = query_start;
@@ -1591,7 +1639,7 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     int lds_max = 0;
     st = lds_limit(&lds_max);
     if (st != PA_OK) return st;
-    if (decode_dynamic_lds(num_seqs, multi) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
+    if (decode_dynamic_lds(num_seqs, multi, plan.slice) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
 
     hipStream_t sm = static_cast<hipStream_t>(stream);
     if (!multi) {

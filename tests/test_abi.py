@@ -139,10 +139,11 @@ def test_attend_workspace_sizes():
     L = pa.lib()
     d = _desc(head_dim=128, num_kv_heads=8)
     W_, S, D, Hkv = 100, 64, 128, 8
+    waves = W_ * 2  # a worker has a wave per kv-head of a slice: 2 of the 8 kv-heads here
     r = lambda x: (x + 255) // 256 * 256
     for Hq, cols in [(32, 16), (56, 14), (8, 16), (128, 16)]:  # G = 4, 7, 1, 16: floor(16/G) tokens x G heads
         got = L.pa_attend_workspace_bytes(S, Hq, 256, ctypes.byref(d), W_)
-        assert got == r(8 * S * Hkv) + r(4 * W_ * 2 * cols) + 4 * W_ * 2 * cols * D
+        assert got == r(8 * S * Hkv) + r(4 * waves * 2 * cols) + 4 * waves * 2 * cols * D
     assert L.pa_attend_workspace_bytes(S, 32, 256, ctypes.byref(d), -1) == 0
 
 
@@ -174,14 +175,18 @@ def test_decode_zero_sequences_is_a_noop():
 def test_workspace_sizes():
     L = pa.lib()
     d = _desc(head_dim=128, num_kv_heads=8)
-    # one wavefront per (sequence, kv-head): no workspace
+    # one worker per (sequence, kv-head slice): no workspace
     assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), -1) == 0
     # stream split: an 8-byte arrival word per (sequence, kv-head), then
-    # 2 parts per worker of G lse values and G*D outputs
-    W, S, G, D, Hkv = 100, 64, 4, 128, 8
-    got = L.pa_decode_workspace_bytes_ex(S, 32, 256, ctypes.byref(d), W)
+    # 2 parts per wave of G lse values and G*D outputs; a worker has a wave
+    # per kv-head of its slice (the largest divisor of Hkv up to 2)
     r = lambda x: (x + 255) // 256 * 256
-    assert got == r(8 * S * Hkv) + r(4 * W * 2 * G) + 4 * W * 2 * G * D
+    for Hkv, Hq, sl in [(8, 32, 2), (4, 28, 2), (6, 24, 2), (16, 32, 2), (2, 4, 2), (7, 14, 1), (3, 3, 1), (1, 16, 1)]:
+        d = _desc(head_dim=128, num_kv_heads=Hkv)
+        W, S, G, D = 100, 64, Hq // Hkv, 128
+        got = L.pa_decode_workspace_bytes_ex(S, Hq, 256, ctypes.byref(d), W)
+        assert got == r(8 * S * Hkv) + r(4 * W * sl * 2 * G) + 4 * W * sl * 2 * G * D, (Hkv, Hq)
+    d = _desc(head_dim=128, num_kv_heads=8)
     # rejected shapes report 0
     assert L.pa_decode_workspace_bytes_ex(64, 33, 256, ctypes.byref(d), W) == 0
 

@@ -88,6 +88,9 @@ SMALL = [
     dict(S=6, Hq=4, Hkv=4, D=64, B=16, dtype="f32", ctx=[0, 0, 0, 1, 0, 2]),
     dict(S=1, Hq=5, Hkv=1, D=64, B=16, dtype="bf16", ctx=[3000]),
     dict(S=40, Hq=2, Hkv=1, D=128, B=16, dtype="f16", ctx_range=(1, 40), max_blocks_per_seq=9),
+    dict(S=5, Hq=24, Hkv=12, D=64, B=16, dtype="bf16", ctx_range=(1, 400)),  # six slices of 2 kv-heads
+    dict(S=3, Hq=32, Hkv=16, D=128, B=32, dtype="f16", ctx_range=(1, 500)),  # eight slices of 2 kv-heads
+    dict(S=4, Hq=12, Hkv=6, D=64, B=16, dtype="f32", ctx_range=(1, 300)),  # three slices of 2 kv-heads
 ]
 
 
