@@ -60,7 +60,10 @@ constexpr int kMaxGroup = 16;
 #define PA_WAVES_PER_CU 2
 #endif
 constexpr int kWavesPerCU = PA_WAVES_PER_CU;  // automatic split: decode waves per compute unit
-constexpr int kMinBlocksPerWorker = 16;
+#ifndef PA_MIN_BLOCKS_PER_WORKER
+#define PA_MIN_BLOCKS_PER_WORKER 16
+#endif
+constexpr int kMinBlocksPerWorker = PA_MIN_BLOCKS_PER_WORKER;
 constexpr int kMaxWorkers = 1 << 20;
 constexpr int kMaxRopePairs = 64;  // head_dim / 2
 #ifndef PA_RUN_COST_BYTES
@@ -1485,8 +1488,14 @@ pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
         int cus = 0;
         pa_status_t st = cu_count(&cus);
         if (st != PA_OK) return st;
+        // At least kMinBlocksPerWorker blocks per worker, counted on the widest
+        // table; but never fewer workers than (sequence, slice) items, since a
+        // worker that walks several sequences pays a run start (a Q load and a
+        // first tile that waits a full memory latency) for each in turn.
         const int64_t units_bound = (int64_t)num_seqs * plan->chunks * max_blocks;
         int64_t want = (units_bound + kMinBlocksPerWorker - 1) / kMinBlocksPerWorker;
+        const int64_t items = (int64_t)num_seqs * plan->chunks;
+        if (want < items) want = items;
         const int64_t per_cu = kWavesPerCU / plan->slice;
         const int64_t cap = (int64_t)cus * (per_cu < 1 ? 1 : per_cu);
         W = (int)(want < 1 ? 1 : (want > cap ? cap : want));
