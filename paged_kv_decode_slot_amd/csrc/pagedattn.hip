@@ -677,9 +677,12 @@ __device__ inline float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_offset
 // log-sum-exps, so a merge of up to PB parts costs one round trip to memory.  Only the first
 // `active` columns are stored (the rest pad the last token group).
 #ifndef PA_MERGE_LOADS
-#define PA_MERGE_LOADS 16
+#define PA_MERGE_LOADS 8
 #endif
-constexpr int kMergeLoads = PA_MERGE_LOADS;  // 16-byte loads per lane in one batch of a merge
+// 16-byte loads per lane in one batch of a merge.  Larger batches shorten
+// merges of many parts but raise the kernel's register count everywhere.
+constexpr int kMergeLoads = PA_MERGE_LOADS;
+static_assert(kMergeLoads >= 8, "a batch must hold at least one part at 8 units per lane");
 
 template <int DT, int D, int UPL, bool MQ>
 __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, int s, int kvh, int row0, int active, int64_t F, int parts,
