@@ -353,9 +353,6 @@ __device__ inline int64_t owner_of(int64_t u, int64_t U, int64_t W) { return ((u
 __device__ inline void coherent_store(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline float coherent_load(const float* p) {
-    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // All of this wave's outstanding vector-memory operations (stores included) complete.
 // s_waitcnt immediate for vmcnt(0) alone (expcnt 7 and lgkmcnt 15 wait for
 // nothing).  Issued through the builtin, the compiler sees the wait and knows
