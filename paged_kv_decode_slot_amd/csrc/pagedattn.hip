@@ -399,11 +399,6 @@ typedef const int32_t __attribute__((address_space(4)))* ScalarPtr;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// A 16-byte store with the non-temporal hint.
-__device__ inline void store_nt(uint8_t* p, uint4 v) {
-    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
-}
-
 template <typename T>
 __device__ inline T load_kv(const uint8_t* p) {
 #if PA_KV_NONTEMPORAL
@@ -638,18 +633,10 @@ __device__ inline float wave_sum(float x) {
     return row_group_sum(x);
 }
 
-// Combine the parts of a split (sequence, kv-head) by log-sum-exp and write out.
-// Parts are the workers whose runs cover units [F, F + nb): with W >= U each
-// unit is its own run; otherwise they are owner(F) .. owner(F + nb - 1), all
-// in slot 0 except the first when its run began in an earlier pair.
-// Parts are taken 64 at a time: lanes read the 64 parts' log-sum-exps at once
-// (the maximum and the weights follow by wave reductions); then the (pass,
-// part) items of the chunk are read kBatch at a time, each lane loading two
-// output dims of one head per item, and accumulated in LDS.
-// Partial results read through buffer resources: loads are bounds-checked to
+// Partial results go through buffer resources: accesses are bounds-checked to
 // the resource (a load past its end returns 0) and carry the agent-coherence
-// bit (the cache-policy operand's SC1, 16), like the relaxed agent-scope loads
-// above.  Word 3 is the gfx9-family raw-buffer format.
+// bit (the cache-policy operand's SC1, 16), like the relaxed agent-scope
+// accesses above.  Word 3 is the gfx9-family raw-buffer format.
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kCoherentPolicy = 16;
 __device__ inline f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, int byte_offset) {
@@ -1078,11 +1065,12 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
 // new K/V rows of RPW consecutive (sequence, kv-head) rows into their slots,
 // the same bytes pa_write_kv stores.  It runs beside the attention waves, so
 // their loads never wait behind these stores (a wave's loads and stores share
-// one counter).  The stores carry the non-temporal hint: each row touches one
-// line per 16-byte K piece and one per V line of its slab, and letting those
-// partial lines stream out instead of sitting dirty in L2 costs the reads
-// around them less.  A row with no context, or whose block id or length lies
-// outside the table or pool, is skipped.
+// one counter).  Each row touches one line per 16-byte K piece and one per V
+// line of its slab.  These partial-line stores are what the append costs the
+// reads around them.  Plain stores cost the most; the non-temporal hint less;
+// the agent-coherence bit (SC1), used here, a little less again.  A row with
+// no context, or whose block id or length lies outside the table or pool, is
+// skipped.
 template <int DT, int D, int B, bool ROPE>
 __device__ __attribute__((always_inline)) void store_new_rows(const DecodeArgs& a, int wi, const double* rw) {
     using C = Cfg<DT, D, B>;
@@ -1091,6 +1079,11 @@ __device__ __attribute__((always_inline)) void store_new_rows(const DecodeArgs& 
     constexpr int RPW = 64 / KP;    // rows per wave: one piece per lane
     constexpr int NV = RPW * D / 64;  // V elements per lane; element k of a lane is in row 64k / D
     const int lane = threadIdx.x & 63;
+    // Stores go through a resource over the row's 16-token slab, with the
+    // agent-coherence bit.
+    auto slab_rsrc = [](uint8_t* p) {
+        return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, Cfg<DT, D, B>::kSlabBytes, kBufferWord3);
+    };
     const int Hkv = a.num_kv_heads;
     const int rows = a.num_seqs * Hkv;
     const int r0 = wi * RPW;
@@ -1151,7 +1144,9 @@ __device__ __attribute__((always_inline)) void store_new_rows(const DecodeArgs& 
             }
             kv = lo ? float_to_piece<DT>(x) : float_to_piece<DT>(y);
         }
-        if (slab >= 0) store_nt(a.k_cache_w + slab + (ki * 16 + tt) * 16, kv);
+        if (slab >= 0)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, kv), slab_rsrc(a.k_cache_w + slab),
+                                                   (ki * 16 + tt) * 16, 0, kCoherentPolicy);
     }
     // V: element k of the lane is dim (64k) % D + lane of row r0 + 64k / D.
     constexpr int Y = 4 / E;
@@ -1165,9 +1160,11 @@ __device__ __attribute__((always_inline)) void store_new_rows(const DecodeArgs& 
             const int d = (64 * k) % D + lane;
             const int e = ((((tt / 4) * (D / (16 * Y)) + d / (16 * Y)) * 16 + d % 16) * Y + (d / 16) % Y) * 4 + tt % 4;
             if constexpr (E == 2)
-                __builtin_nontemporal_store((uint16_t)vv[k], reinterpret_cast<uint16_t*>(a.v_cache_w + slab) + e);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)vv[k], slab_rsrc(a.v_cache_w + slab), e * 2, 0,
+                                                      kCoherentPolicy);
             else
-                __builtin_nontemporal_store(vv[k], reinterpret_cast<uint32_t*>(a.v_cache_w + slab) + e);
+                __builtin_amdgcn_raw_buffer_store_b32(vv[k], slab_rsrc(a.v_cache_w + slab), e * 4, 0,
+                                                      kCoherentPolicy);
         }
     }
 }
