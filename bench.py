@@ -140,6 +140,8 @@ def measure(n, args, device):
     decode_ms = time_back_to_back([s[1] for s in steps], K, Wm)
     pairs = [(lambda w=w, d=d: (w(), d())) for (w, d, _) in steps]
     two_ms = time_back_to_back(pairs, K, Wm)
+    # Hot cache: one layer's pools over and over (whatever of them the 256 MB MALL keeps).
+    hot_ms = time_back_to_back([steps[0][2]], K, Wm)
     (t_step,) = time_each([[s[2]] for s in steps], K, Wm)
     t_write, t_decode = time_each([[s[0], s[1]] for s in steps], K, Wm)
     dec_b, wr_b, st_b = W.decode_bytes(case), W.write_bytes(case), W.step_bytes(case)
@@ -165,6 +167,7 @@ def measure(n, args, device):
         t_decode_us_events=dict(mean=statistics.fmean(t_decode), p10=pct(t_decode, 10), p50=pct(t_decode, 50),
                                 p90=pct(t_decode, 90)),
         t_write_us_events=dict(mean=statistics.fmean(t_write), p50=pct(t_write, 50)),
+        hot_step_us=hot_ms * 1e3 / K,
     )
 
 
@@ -330,12 +333,15 @@ def measure_norm(args, device):
 TRAFFIC_FILES = {(3, "fused"): "profiles/decode_append_kernel_C3_llama3-8b_bf16_counters.txt",
                  (3, "decode"): "profiles/decode_kernel_C3_llama3-8b_bf16_counters.txt",
                  (3, "attend4"): "profiles/attend_kernel_C3_llama3-8b_4tokens_bf16_counters.txt",
-                 (3, "rope"): "profiles/decode_rope_append_kernel_C3_llama3-8b_bf16_counters.txt"}
+                 (3, "rope"): "profiles/decode_rope_append_kernel_C3_llama3-8b_bf16_counters.txt",
+                 (4, "fused"): "profiles/decode_append_kernel_C4_ragged_bf16_counters.txt",
+                 (5, "fused"): "profiles/decode_append_kernel_C5_long_bf16_counters.txt"}
 KERNEL_SOURCE = "paged_kv_decode_slot_amd/csrc/pagedattn.hip"
 
 
-def measured_traffic(config: int, kind: str):
-    """Bytes per launch from a counter summary, or None if there is none or the kernel changed since."""
+def measured_counters(config: int, kind: str):
+    """{"fetch", "write", "total"} bytes per launch from a counter summary, or None if
+    there is none or the kernel source changed since it was taken."""
     import hashlib
 
     path = TRAFFIC_FILES.get((config, kind))
@@ -349,7 +355,65 @@ def measured_traffic(config: int, kind: str):
     src = hashlib.sha256(open(os.path.join(ROOT, KERNEL_SOURCE), "rb").read()).hexdigest()
     if fields.get("source_sha256") != src or "traffic_bytes_per_launch" not in fields:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    fetch, write = [int(x.split()[-1]) for x in fields["scaled bytes per launch"].split(",")]
+    return dict(fetch=fetch, write=write, total=int(fields["traffic_bytes_per_launch"]))
+
+
+def measured_traffic(config: int, kind: str):
+    """Counter bytes (read + written) per launch, or None."""
+    c = measured_counters(config, kind)
+    return None if c is None else c["total"]
+
+
+def kv_share(case, config: int, kind: str):
+    """Algorithmic K/V bytes read over the counter-measured bytes fetched (1.0: no K/V
+    byte fetched twice and nothing else fetched), or None without counters."""
+    from paged_kv_decode_slot_amd import workloads as W
+
+    c = measured_counters(config, kind)
+    return None if c is None else round(W.kv_read_bytes(case) / c["fetch"], 4)
+
+
+def measure_ceilings(device, args):
+    """Read-bandwidth ceilings on this GPU, measured with pa_read_probe over a 4 GiB
+    buffer (16 times the MALL): every byte in address order, and whole 4 KB tiles
+    in a shuffled order (how the decode reads a paged pool).  Context for the
+    decode's fraction of peak, not a target."""
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=device)
+    buf.fill_(0x01020304)
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    waves = 32 * cus
+    g = torch.Generator(device="cpu").manual_seed(0)
+    res = {}
+    for name, tile, order in (("stream_read", 4096, None), ("random_4k_tiles", 4096, "perm")):
+        ids = None
+        if order == "perm":
+            ids = torch.randperm(nbytes // tile, generator=g).to(torch.int32).to(device)
+        call, _sink = pa.prepare_read_probe(buf, tile, ids, num_waves=waves)
+        ms = time_back_to_back([call], max(5, args.steps // 10), 2)
+        us = ms * 1e3 / max(5, args.steps // 10)
+        res[name] = dict(gbs=round(nbytes / (us * 1e-6) / 1e9, 1), us=round(us, 1),
+                         frac_of_peak=round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4))
+        del ids
+    del buf
+    res["note"] = ("pa_read_probe over 4 GiB, 16-byte non-temporal loads, %d wavefronts; tile ids read from "
+                   "memory in the shuffled case" % waves)
+    return res
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(case, min_seconds):
@@ -369,7 +433,7 @@ def cpu_baseline(case, min_seconds):
         reps += 1
     per_step = t_total / reps
     gbs = W.step_bytes(case) / per_step / 1e9
-    return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle",
+    return dict(value=round(gbs, 4), unit="GB/s", cores=threads, kind="oracle", cpu_model=cpu_model(),
                 sample=f"the whole workload (append + decode of all {case.S} sequences), {reps} reps, "
                        f"{per_step * 1e3:.1f} ms per step, float64 C oracle")
 
@@ -380,7 +444,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, help="workload 1-5 (default 3)")
-    ap.add_argument("--also", default="4", help="comma list of extra workloads reported under 'other'")
+    ap.add_argument("--also", default="1,2,4,5", help="comma list of extra workloads reported under 'other'")
     ap.add_argument("--layers", type=int, default=0, help="distinct K/V pools to rotate over (0: enough for 2 GiB)")
     ap.add_argument("--workers", type=int, default=0, help="decode work split (0 automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -391,6 +455,7 @@ def main():
                     help="also time the step with the rotary embedding fused in, at this base (0: skip)")
     ap.add_argument("--no-pool", action="store_true", help="skip the block-pool leg")
     ap.add_argument("--no-norm", action="store_true", help="skip the RMSNorm leg")
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the read-bandwidth ceilings")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="first run one plain device copy of this many MiB (a known-size kernel for counter scaling)")
     args = ap.parse_args()
@@ -433,8 +498,10 @@ def main():
             decode_us=round(r["decode_us_mean"], 2), decode_gbs=round(r["decode_gbs"], 1),
             decode_frac_of_peak=round(r["decode_gbs"] / PEAK_HBM_GBS, 4),
             two_call_us=round(r["two_call_ms_per_step"] * 1e3, 2),
+            hot_step_us=round(r["hot_step_us"], 2),
             seq_heads_per_s=round(r["seq_heads_per_s"]), layers=r["layers"],
-            step_bytes=r["step_bytes"], context_tokens=int(c.context_lens.sum()))
+            step_bytes=r["step_bytes"], decode_bytes=r["decode_bytes"], context_tokens=int(c.context_lens.sum()),
+            traffic=measured_traffic(n, "fused"), kv_share=kv_share(c, n, "fused"))
         del c, r
         torch.cuda.empty_cache()
 
@@ -451,6 +518,11 @@ def main():
     norm = None
     if not args.no_norm:
         norm = measure_norm(args, device)
+        torch.cuda.empty_cache()
+
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(device, args)
         torch.cuda.empty_cache()
 
     pool = None
@@ -494,6 +566,7 @@ def main():
             "frac": round(main_res["step_gbs"] / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic(args.config, "fused"),
             "traffic_unit": "bytes per launch",
+            "kv_share": kv_share(case, args.config, "fused"),
             "bytes_per_launch": step_bytes,
             "launch_us_mean": round(main_res["step_us_mean"], 2),
             "timing": "HIP events around the K back-to-back launches on the launch stream",
@@ -502,6 +575,8 @@ def main():
         "detail": {
             "seq_heads_per_s": round(main_res["seq_heads_per_s"]),
             "step_bytes": step_bytes,
+            "hot_step_us": round(main_res["hot_step_us"], 2),
+            "ceilings": ceilings,
             "step_us_per_launch_events": r2(main_res["step_us_events"]),
             "decode_alone": {
                 "us": round(main_res["decode_us_mean"], 2),

@@ -43,6 +43,14 @@
  * that a matrix-core operand needs in one load, with consecutive lanes
  * reading consecutive bytes, and keeps a token's V row inside one quarter of
  * its slab.  A slot is p * block_size + o.
+ * The geometry per (block, kv-head) is that of a plain
+ * [num_blocks][num_kv_heads][block_size][head_dim] pool -- the same bytes,
+ * the same tile per (block, kv-head) -- but the order of the elements inside
+ * each 16-token slab is this one, not token-major rows: with token-major
+ * rows a V operand (4 consecutive tokens of one dim) would take 4 separate
+ * 2- or 4-byte loads per lane.  Pools are therefore written only through
+ * pa_write_kv / pa_decode_append (or code that follows the formulas above);
+ * a caller holding token-major pools must convert them once.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -54,7 +62,19 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
+
+/*
+ * Every workspace begins with this many bytes of synchronisation words (the
+ * counters by which the parts of a split are merged inside one launch).
+ * They must hold zero before the workspace is first used -- one hipMemset
+ * (or a zero-filled allocation) when it is created -- and every call leaves
+ * them zero again when it completes, so a workspace may then be reused by
+ * calls of any shape, and captured in a graph, without clearing it again.
+ * The bytes after them need no initialisation.  Calls that share a workspace
+ * must not run at the same time (issue them on one stream).
+ */
+#define PA_WORKSPACE_SYNC_BYTES (256 * 1024)
 
 typedef enum pa_status {
     PA_OK = 0,
@@ -111,7 +131,9 @@ pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slo
  *   context_lens  : int32 [num_seqs], 4-byte aligned
  *   workspace     : device scratch of at least pa_decode_workspace_bytes(...)
  *                   bytes, 256-byte aligned (may be NULL when that is 0);
- *                   its contents need no initialisation and are clobbered
+ *                   its first PA_WORKSPACE_SYNC_BYTES bytes must be zero
+ *                   before its first use and are left zero by every call;
+ *                   the rest needs no initialisation and is clobbered
  * Supported: 1 <= G <= 16, head_dim 64/128, block_size 16/32, num_seqs <= 4096.
  * Preconditions (unchecked): 0 <= L <= max_blocks_per_seq * block_size and
  * 0 <= block_tables[s][j] < num_blocks for j < ceil(L / block_size).
@@ -141,7 +163,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  *                       between runs are merged by a log-sum-exp reduction
  * A worker is one workgroup with a wavefront per kv-head of a slice of the
  * kv-heads (the slice is the largest divisor of num_kv_heads up to 2), so
- * every wave of a worker covers the same logical blocks.
+ * every wave of a worker covers the same logical blocks.  num_workers times
+ * the slice may be at most PA_WORKSPACE_SYNC_BYTES / 8 - 8 (the arrival words
+ * of the split), else PA_ERR_UNSUPPORTED.
  * Every choice computes the same function; results agree within rounding.
  */
 pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -215,9 +239,12 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
  *   out[row][h][:] = sum_{t <= L-n+i} softmax_t(scale * q[row][h][:] . K_t) * V_t
  * The K/V of all L positions, the query tokens' own included, must already be
  * in the cache (pa_write_kv).  n = 1 for every sequence is exactly pa_decode_ex.
- *   q, out         : [query_start[num_seqs]][num_q_heads][head_dim], 16-byte aligned
- *   query_start    : int32 [num_seqs + 1], device, non-decreasing from 0
+ *   q, out         : [num_q_rows][num_q_heads][head_dim], 16-byte aligned
+ *   query_start    : int32 [num_seqs + 1], device, non-decreasing from 0 to
+ *                    at most num_q_rows; values outside [0, num_q_rows] are
+ *                    clamped into it, so no row outside q/out is touched
  *   max_query_len  : host value >= every n (0: nothing to do)
+ *   num_q_rows     : host value, the rows of q and out
  *   other arguments as in pa_decode_ex; the workspace must hold
  *   pa_attend_workspace_bytes(...) bytes
  * Query tokens are taken floor(16 / G) at a time (one launch per group of
@@ -229,8 +256,8 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
 pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
                       int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_query_len,
-                      const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes, int32_t num_workers,
-                      pa_stream_t stream);
+                      int32_t num_q_rows, const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
+                      int32_t num_workers, pa_stream_t stream);
 
 /* Workspace bytes pa_attend needs for these shapes and num_workers (0 for arguments it rejects). */
 size_t pa_attend_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
@@ -239,6 +266,9 @@ size_t pa_attend_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
 /* Workspace bytes pa_decode_ex and pa_decode_append need for that num_workers. */
 size_t pa_decode_workspace_bytes_ex(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                     const pa_cache_desc_t* cache, int32_t num_workers);
+
+/* PA_WORKSPACE_SYNC_BYTES of the built library. */
+size_t pa_workspace_sync_bytes(void);
 
 /* Static, human-readable name of a status. */
 const char* pa_status_string(pa_status_t status);
@@ -362,6 +392,23 @@ pa_status_t pa_pool_telemetry(const pa_pool_acct_t* acct, const int32_t* state_h
  */
 pa_status_t pa_rmsnorm(const void* x, void* residual, const void* weight, void* out, int64_t rows, int32_t hidden,
                        float eps, int32_t dtype, pa_stream_t stream);
+
+/*
+ * Read-bandwidth probe (a measurement aid, not part of the attention path):
+ * the decode is a scan of K/V tiles, memory-bound (LLM-Inference-Engine
+ * README, "why dynamic injection" paragraph and key learnings), and this call
+ * measures the ceilings it is judged against.  It reads num_tiles tiles of
+ * tile_bytes bytes from src -- tile i at (tile_ids ? tile_ids[i] : i) *
+ * tile_bytes -- with 16-byte loads, and stores into sink, per lane of each of
+ * num_waves wavefronts, the XOR of the 16-byte pieces it read (the XOR over
+ * all of sink is the XOR over all pieces read).
+ *   src      : device, 16-byte aligned;  tile_ids : int32 [num_tiles], device, or NULL
+ *   sink     : device, num_waves * 64 * 16 bytes, 16-byte aligned, written
+ *   tile_bytes : a positive multiple of 1024;  num_waves : a positive multiple of 4
+ * Precondition (unchecked): every tile lies inside src.
+ */
+pa_status_t pa_read_probe(const void* src, const int32_t* tile_ids, int64_t num_tiles, int32_t tile_bytes,
+                          uint32_t* sink, int32_t num_waves, pa_stream_t stream);
 
 /* PA_ABI_VERSION of the built library. */
 int32_t pa_abi_version(void);

@@ -21,7 +21,9 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# PA_ORACLE_LIB selects another build of the same source (the sanitizer test builds one).
+_LIB_OVERRIDE = os.environ.get("PA_ORACLE_LIB")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _lib = None
 
@@ -38,7 +40,7 @@ def build() -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        if not _LIB_OVERRIDE and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
             build()
         lib = ctypes.CDLL(_LIB)
         P, I, I64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64

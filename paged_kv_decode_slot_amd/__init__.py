@@ -29,10 +29,12 @@ from .binding import (  # noqa: F401
     lib,
     library_path,
     new_cache,
+    new_workspace,
     prepare_attend,
     prepare_decode,
     prepare_decode_append,
     prepare_decode_rope_append,
+    prepare_read_probe,
     prepare_write_kv,
     rope,
     workspace_bytes,

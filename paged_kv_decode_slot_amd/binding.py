@@ -39,6 +39,8 @@ EXPORTS = (
     "pa_acct_retire",
     "pa_pool_telemetry",
     "pa_rmsnorm",
+    "pa_read_probe",
+    "pa_workspace_sync_bytes",
     "pa_status_string",
     "pa_abi_version",
 )
@@ -102,7 +104,7 @@ def lib() -> ctypes.CDLL:
         L.pa_decode_ex.restype = ctypes.c_int
         L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, I32, P]
         L.pa_decode_append.restype = ctypes.c_int
-        L.pa_attend.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, I32, DP, P, SZ, I32, P]
+        L.pa_attend.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, I32, I32, DP, P, SZ, I32, P]
         L.pa_attend.restype = ctypes.c_int
         L.pa_attend_workspace_bytes.argtypes = [I32, I32, I32, DP, I32]
         L.pa_rope.argtypes = [P, P, P, I32, I32, I32, I32, I32, ctypes.c_float, P]
@@ -119,6 +121,10 @@ def lib() -> ctypes.CDLL:
         L.pa_status_string.restype = ctypes.c_char_p
         L.pa_abi_version.argtypes = []
         L.pa_abi_version.restype = I32
+        L.pa_read_probe.argtypes = [P, P, ctypes.c_int64, I32, P, I32, P]
+        L.pa_read_probe.restype = ctypes.c_int
+        L.pa_workspace_sync_bytes.argtypes = []
+        L.pa_workspace_sync_bytes.restype = SZ
         L.pa_rmsnorm.argtypes = [P, P, P, P, ctypes.c_int64, I32, ctypes.c_float, I32, P]
         L.pa_rmsnorm.restype = ctypes.c_int
         L.pa_pool_init.argtypes = [P, P, I32, I32, P]
@@ -191,6 +197,34 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+# Workspaces start zero-filled: their first pa_workspace_sync_bytes() bytes are the
+# library's synchronisation words, which must be zero before the first call and
+# which every call leaves zero.  One workspace per (device, stream) is kept and
+# grown for the calls that do not bring their own; calls on one stream never
+# overlap, so they can share it.
+_WS_CACHE: dict = {}
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled uint8 workspace of nbytes (at least 1), ready for any call."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _workspace(dev: torch.device, need: int, workspace, own: bool) -> torch.Tensor:
+    if workspace is not None:
+        if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the same device")
+        return workspace
+    if own:  # a prepared call keeps its own (it may be captured in a graph)
+        return new_workspace(need, dev)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _WS_CACHE.get(key)
+    if ws is None or ws.numel() < need:
+        ws = new_workspace(max(need, 2 * (0 if ws is None else ws.numel())), dev)
+        _WS_CACHE[key] = ws
+    return ws
+
+
 def _dev(*ts: torch.Tensor) -> torch.device:
     d = ts[0].device
     if d.type != "cuda":
@@ -232,7 +266,8 @@ def workspace_bytes(num_seqs: int, num_q_heads: int, max_blocks_per_seq: int, de
                                                   ctypes.byref(desc), num_workers))
 
 
-def _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_workers, workspace):
+def _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_workers, workspace,
+                 own_workspace=False):
     desc = cache_desc(k_cache, v_cache)
     dev = _dev(q, k_cache, v_cache, block_tables, context_lens)
     if q.dim() != 3 or q.shape[2] != desc.head_dim or q.dtype != k_cache.dtype or not q.is_contiguous():
@@ -249,10 +284,7 @@ def _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out, nu
         raise ValueError("out must be contiguous and shaped like q")
     maxblk = int(block_tables.shape[1])
     need = workspace_bytes(S, Hq, maxblk, desc, num_workers)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    elif workspace.device != dev or workspace.dtype != torch.uint8:
-        raise ValueError("workspace must be a uint8 tensor on the same device")
+    workspace = _workspace(dev, need, workspace, own_workspace)
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
             ctypes.c_float(scale), out.data_ptr(), S, Hq, maxblk, ctypes.byref(desc), workspace.data_ptr(),
             workspace.numel(), int(num_workers), _stream(dev))
@@ -266,7 +298,9 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
 
     num_workers: 0 automatic, -1 one worker per (sequence, kv-head slice), >0 that many
     workers (a worker is a workgroup with one wavefront per kv-head of a slice).
-    workspace: optional uint8 device tensor; one is allocated when not given.
+    workspace: optional uint8 device tensor whose first pa_workspace_sync_bytes() bytes
+    are zero before its first use (new_workspace() makes one); when not given, a
+    zero-filled workspace kept for the current stream is used.
     """
     dev, out, args, _keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
                                          num_workers, workspace)
@@ -295,7 +329,7 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=N
     no-argument callable that issues the same pa_decode_ex on the stream that
     is current now, and returns out."""
     _dev_, out, args, keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                                          num_workers, workspace)
+                                          num_workers, workspace, own_workspace=True)
     fn = lib().pa_decode_ex
 
     def call():
@@ -305,9 +339,10 @@ def prepare_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out=N
     return call
 
 
-def _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_workers, workspace):
+def _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, out, num_workers, workspace,
+                 own_workspace=False):
     dev, out, dargs, keep = _decode_args(q, k_cache, v_cache, block_tables, context_lens, scale, out,
-                                         num_workers, workspace)
+                                         num_workers, workspace, own_workspace)
     desc = keep[7]
     S = q.shape[0]
     for t in (k_new, v_new):
@@ -339,7 +374,7 @@ def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, conte
                           num_workers=0, workspace=None):
     """Validate once; return a no-argument callable issuing the same pa_decode_append."""
     _dev_, out, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
-                                          out, num_workers, workspace)
+                                          out, num_workers, workspace, own_workspace=True)
     fn = lib().pa_decode_append
 
     def call():
@@ -350,7 +385,7 @@ def prepare_decode_append(q, k_new, v_new, k_cache, v_cache, block_tables, conte
 
 
 def _attend_args(q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, scale, out,
-                 num_workers, workspace):
+                 num_workers, workspace, own_workspace=False):
     desc = cache_desc(k_cache, v_cache)
     dev = _dev(q, k_cache, v_cache, block_tables, context_lens, query_start)
     if q.dim() != 3 or q.shape[2] != desc.head_dim or q.dtype != k_cache.dtype or not q.is_contiguous():
@@ -370,13 +405,11 @@ def _attend_args(q, k_cache, v_cache, block_tables, context_lens, query_start, m
         raise ValueError("out must be contiguous and shaped like q")
     maxblk = int(block_tables.shape[1])
     need = int(lib().pa_attend_workspace_bytes(S, Hq, maxblk, ctypes.byref(desc), int(num_workers)))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    elif workspace.device != dev or workspace.dtype != torch.uint8:
-        raise ValueError("workspace must be a uint8 tensor on the same device")
+    workspace = _workspace(dev, need, workspace, own_workspace)
     args = (q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(),
             query_start.data_ptr(), ctypes.c_float(scale), out.data_ptr(), S, Hq, maxblk, int(max_query_len),
-            ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), int(num_workers), _stream(dev))
+            int(q.shape[0]), ctypes.byref(desc), workspace.data_ptr(), workspace.numel(), int(num_workers),
+            _stream(dev))
     return dev, out, args, (q, k_cache, v_cache, block_tables, context_lens, out, workspace, desc, query_start)
 
 
@@ -400,7 +433,7 @@ def prepare_attend(q, k_cache, v_cache, block_tables, context_lens, query_start,
                    num_workers=0, workspace=None):
     """Validate once; return a no-argument callable issuing the same pa_attend."""
     _dev_, out, args, keep = _attend_args(q, k_cache, v_cache, block_tables, context_lens, query_start,
-                                          max_query_len, scale, out, num_workers, workspace)
+                                          max_query_len, scale, out, num_workers, workspace, own_workspace=True)
     fn = lib().pa_attend
 
     def call():
@@ -426,9 +459,9 @@ def rope(q: torch.Tensor, k: torch.Tensor, positions: torch.Tensor, rope_theta: 
 
 
 def _rope_append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, rope_theta, out,
-                      num_workers, workspace):
+                      num_workers, workspace, own_workspace=False):
     dev, out, args, keep = _append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
-                                        out, num_workers, workspace)
+                                        out, num_workers, workspace, own_workspace)
     # pa_decode_append arguments: (q, kn, vn, k, v, bt, ctx, scale, out, S, Hq, maxblk, desc, ws, ws_n, wk, st)
     args = args[:8] + (ctypes.c_float(rope_theta),) + args[8:]
     return dev, out, args, keep
@@ -449,7 +482,7 @@ def prepare_decode_rope_append(q, k_new, v_new, k_cache, v_cache, block_tables, 
                                out=None, *, num_workers=0, workspace=None):
     """Validate once; return a no-argument callable issuing the same pa_decode_rope_append."""
     _dev_, out, args, keep = _rope_append_args(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
-                                               scale, rope_theta, out, num_workers, workspace)
+                                               scale, rope_theta, out, num_workers, workspace, own_workspace=True)
     fn = lib().pa_decode_rope_append
 
     def call():
@@ -604,3 +637,32 @@ def prepare_rmsnorm(x, weight, eps, out, residual=None):
         if st:
             _check("pa_rmsnorm", st)
     return call
+
+
+# --- read-bandwidth probe (measurement aid) ---
+
+def prepare_read_probe(src: torch.Tensor, tile_bytes: int, tile_ids: torch.Tensor | None = None,
+                       num_waves: int = 8192):
+    """A no-argument callable that reads src's tiles of tile_bytes (in tile_ids order, or
+    address order) with pa_read_probe, and the sink tensor it writes: returns (call, sink)."""
+    dev = _dev(src) if tile_ids is None else _dev(src, tile_ids)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if tile_ids is None:
+        num_tiles = nbytes // tile_bytes
+    else:
+        if tile_ids.dtype != torch.int32 or tile_ids.dim() != 1 or not tile_ids.is_contiguous():
+            raise ValueError("tile_ids must be contiguous int32 [n]")
+        num_tiles = tile_ids.shape[0]
+    sink = torch.empty(num_waves * 64 * 4, dtype=torch.int32, device=dev)
+    args = (src.data_ptr(), None if tile_ids is None else tile_ids.data_ptr(), num_tiles, tile_bytes,
+            sink.data_ptr(), num_waves, _stream(dev))
+    fn = lib().pa_read_probe
+
+    def call():
+        st = fn(*args)
+        if st:
+            _check("pa_read_probe", st)
+    call.num_tiles = num_tiles
+    return call, sink

@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("pagedattn.hip", "blockpool.hip", "rmsnorm.hip")]
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("pagedattn.hip", "blockpool.hip", "rmsnorm.hip", "probe.hip")]
 HEADER = os.path.join(ROOT, "include", "pagedattn.h")
 LIB = os.path.join(PKG, "libpagedattn.so")
 

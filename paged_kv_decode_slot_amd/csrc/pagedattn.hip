@@ -41,6 +41,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstring>
 #include <type_traits>
 
 #include "pagedattn.h"
@@ -64,6 +65,11 @@ constexpr int kWavesPerCU = PA_WAVES_PER_CU;  // automatic split: decode waves p
 #define PA_MIN_BLOCKS_PER_WORKER 16
 #endif
 constexpr int kMinBlocksPerWorker = PA_MIN_BLOCKS_PER_WORKER;
+// Synchronisation words at the start of every workspace (zero before the first
+// call, and left zero by every call): kSyncHeader counters, then one arrival
+// word per (range, wave) of a split.
+constexpr int kSyncWords = PA_WORKSPACE_SYNC_BYTES / 8;
+constexpr int kSyncHeader = 8;
 constexpr int kMaxWorkers = 1 << 20;
 constexpr int kMaxRopePairs = 64;  // head_dim / 2
 #ifndef PA_RUN_COST_BYTES
@@ -220,7 +226,7 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     uint8_t* out;
-    unsigned long long* arrivals;  // [num_seqs * Hkv]: (call tag << 32) | parts stored so far
+    unsigned long long* sync;      // the workspace's synchronisation words (see kSyncWords)
     float* part_lse;               // [workers * slice][2][cols]: per wave, two slots
     float* part_o;                 // [workers * slice][2][cols][D]
     const uint8_t* k_new;          // append: [num_seqs][Hkv][D], the token at position ctx-1
@@ -228,7 +234,6 @@ struct DecodeArgs {
     uint8_t* k_cache_w;            // append: the same pools, written
     uint8_t* v_cache_w;
     float scale_log2;
-    uint32_t tag;  // nonzero; differs between consecutive calls
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -243,6 +248,7 @@ struct DecodeArgs {
     int32_t run_cost;     // extra units counted per (sequence, slice) with context (see load_lengths)
     int32_t cols;         // columns of a pair: G heads, or (several query tokens) tpc tokens x G heads
     const int32_t* query_start;  // several query tokens: [num_seqs + 1] query rows of each sequence
+    int32_t num_q_rows;   // several query tokens: rows of q and out (query_start values are clamped to it)
     int32_t chunk;        // several query tokens: this launch takes tokens [chunk*tpc, (chunk+1)*tpc) of each
     int32_t tpc;          // several query tokens: tokens per pair (16 / G)
     double rope_w[kMaxRopePairs];  // append with rotary embedding: frequencies theta^(-2i/D), i < D/2
@@ -295,7 +301,9 @@ __device__ __attribute__((always_inline)) void load_lengths(const DecodeArgs& a,
     for (int i = lo; i < hi; ++i) {
         int c = clamp_ctx(a.context_lens[i], B, a.max_blocks);
         if constexpr (MQ) {
-            const int q0 = a.query_start[i], n = a.query_start[i + 1] - q0;
+            // Rows outside [0, num_q_rows) are never touched, whatever query_start holds.
+            const int q0 = min(max(a.query_start[i], 0), a.num_q_rows);
+            const int n = min(max(a.query_start[i + 1], q0), a.num_q_rows) - q0;
             const int i0 = a.chunk * a.tpc;
             const int nr = i0 < n ? min(a.tpc, n - i0) : 0;
             c = nr > 0 ? max(0, min(c, c - n + i0 + nr)) : 0;
@@ -362,23 +370,14 @@ __device__ inline void wait_vmem_done() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0
 __device__ inline void wait_stores_done() { wait_vmem_done(); }
 
 // Count this wave's part of a split (sequence, kv-head); true for the wave
-// that stores the last part.  The word holds (tag << 32) | parts counted; a
-// word carrying another call's tag (an earlier call, or uninitialised memory)
-// is first claimed for this call by a compare-exchange that also counts this
-// part; every other part is one fetch-add, so simultaneous arrivals never
-// retry each other.  The last part clears the word (tag 0 is never used), so a
-// replay of the same call starts from zero again.  A failed claim means
-// another wave changed the word, so the loop ends after a few rounds.
-__device__ inline bool arrive(unsigned long long* word, uint32_t tag, int parts) {
-    const unsigned long long mine = (unsigned long long)tag << 32;
-    unsigned long long old = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while ((old >> 32) != tag) {
-        const unsigned long long prev = atomicCAS(word, old, mine | 1ull);
-        if (prev == old) return parts == 1;
-        old = prev;
-    }
+// that stores the last part.  The word counts the parts stored so far: it is
+// zero when the call starts (the workspace contract), every part adds one, and
+// the last part puts it back to zero before it merges, so the next call on the
+// same workspace (or a graph replay) finds it zero again.  Nothing depends on
+// what the rest of the workspace holds.
+__device__ inline bool arrive(unsigned long long* word, int parts) {
     const unsigned long long prev = atomicAdd(word, 1ull);
-    if ((int)(prev & 0xffffffffull) + 1 != parts) return false;
+    if ((int)prev + 1 != parts) return false;
     atomicExch(word, 0ull);
     return true;
 }
@@ -1057,7 +1056,11 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
     wait_stores_done();
     const int parts = W >= U ? nb : (int)(owner_of(F + nb - 1, U, W) - owner_of(F, U, W) + 1);
     int last = 0;
-    if (lane == 0) last = arrive(a.arrivals + (size_t)s * a.num_kv_heads + kvh, a.tag, parts) ? 1 : 0;
+    // The pair's arrival word belongs to the range holding its first block: a
+    // pair is split only when it runs past the end of that range, and only the
+    // last pair that starts in a range can, so the word is the pair's alone.
+    const int64_t first_owner = owner_of(F, U, W);
+    if (lane == 0) last = arrive(a.sync + kSyncHeader + first_owner * hs + wi, parts) ? 1 : 0;
     if (__shfl(last, 0)) merge_parts<DT, D, MQ>(a, s, kvh, row0, active, F, Fv, nb, U, W, hs, wi, mlds);
 }
 
@@ -1466,8 +1469,10 @@ int head_slice(int num_kv_heads) {
 }
 
 // Worker count and workspace layout; needs the device only for the automatic choice.
-// Workspace: arrival words [S * Hkv] (8 B each), then part_lse [W * slice][2][cols], then
-// part_o [W * slice][2][cols][D], where cols is a pair's column count (G, or tokens x G).
+// Workspace: the synchronisation words (PA_WORKSPACE_SYNC_BYTES, a fixed size so
+// that calls of any shape find them in the same place), then part_lse
+// [W * slice][2][cols], then part_o [W * slice][2][cols][D], where cols is a
+// pair's column count (G, or tokens x G).
 pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks, const pa_cache_desc_t* cache,
                       int32_t num_workers, int cols, Plan* plan) {
     const int Hkv = cache->num_kv_heads, G = cols, D = cache->head_dim;
@@ -1497,25 +1502,17 @@ pa_status_t make_plan(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks,
         const int64_t cap = (int64_t)cus * (per_cu < 1 ? 1 : per_cu);
         W = (int)(want < 1 ? 1 : (want > cap ? cap : want));
     }
+    // One arrival word per wave of every range must fit the synchronisation words.
+    if ((int64_t)W * plan->slice > kSyncWords - kSyncHeader) return PA_ERR_UNSUPPORTED;
     plan->workers = W;
     const size_t waves = (size_t)W * plan->slice;
-    const size_t arrivals = round_up(sizeof(unsigned long long) * (size_t)num_seqs * Hkv, 256);
+    const size_t sync = PA_WORKSPACE_SYNC_BYTES;
     const size_t lse = round_up(sizeof(float) * waves * 2 * G, 256);
     const size_t o = sizeof(float) * waves * 2 * G * D;
-    plan->off_lse = arrivals;
-    plan->off_o = arrivals + lse;
-    plan->bytes = arrivals + lse + o;
+    plan->off_lse = sync;
+    plan->off_o = sync + lse;
+    plan->bytes = sync + lse + o;
     return PA_OK;
-}
-
-std::atomic<uint32_t> g_call_tag{0x2545f491u};
-
-uint32_t next_tag() {
-    uint32_t t;
-    do {
-        t = g_call_tag.fetch_add(1, std::memory_order_relaxed) + 1;
-    } while (t == 0);
-    return t;
 }
 
 // Dynamic LDS bytes of one decode workgroup: the per-sequence arrays and a
@@ -1576,7 +1573,8 @@ int tokens_per_pair(int num_q_heads, const pa_cache_desc_t* cache) {
 // pa_attend (mode kModeMulti: query_start and max_query_len).
 pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
-                        int32_t max_query_len, float scale, float rope_theta, void* out, int32_t num_seqs,
+                        int32_t max_query_len, int32_t num_q_rows, float scale, float rope_theta, void* out,
+                        int32_t num_seqs,
                         int32_t num_q_heads, int32_t max_blocks_per_seq, const pa_cache_desc_t* cache,
                         void* workspace, size_t workspace_bytes, int32_t num_workers, int mode,
                         pa_stream_t stream) {
@@ -1585,11 +1583,11 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     const bool append = mode_appends(mode), multi = mode == kModeMulti;
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
     if (num_workers < -1 || num_workers > kMaxWorkers) return PA_ERR_INVALID_ARG;
-    if (multi && max_query_len < 0) return PA_ERR_INVALID_ARG;
+    if (multi && (max_query_len < 0 || num_q_rows < 0)) return PA_ERR_INVALID_ARG;
     double rope_w[kMaxRopePairs] = {};
     if (rope_theta != 0.f && !rope_frequencies(rope_theta, cache->head_dim, rope_w)) return PA_ERR_INVALID_ARG;
     // nothing is touched, so empty tensors may pass null pointers
-    if (num_seqs == 0 || (multi && max_query_len == 0)) return PA_OK;
+    if (num_seqs == 0 || (multi && (max_query_len == 0 || num_q_rows == 0))) return PA_OK;
     if (!q || !k_cache || !v_cache || !context_lens || !out) return PA_ERR_INVALID_ARG;
     if (max_blocks_per_seq > 0 && !block_tables) return PA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
@@ -1613,8 +1611,7 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     a.block_tables = block_tables;
     a.context_lens = context_lens;
     a.out = static_cast<uint8_t*>(out);
-    a.arrivals = plan.per_segment ? nullptr : reinterpret_cast<unsigned long long*>(ws);
-    a.tag = next_tag();
+    a.sync = plan.per_segment ? nullptr : reinterpret_cast<unsigned long long*>(ws);
     a.part_lse = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_lse);
     a.part_o = plan.per_segment ? nullptr : reinterpret_cast<float*>(ws + plan.off_o);
     a.k_new = static_cast<const uint8_t*>(k_new);
@@ -1634,6 +1631,7 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     a.per_segment = plan.per_segment;
     a.cols = tpc * G;
     a.query_start = query_start;
+    a.num_q_rows = num_q_rows;
     a.tpc = tpc;
     for (int i = 0; i < kMaxRopePairs; ++i) a.rope_w[i] = rope_w[i];
     // A run start costs about as much as streaming kRunCostBytes of K/V: count
@@ -1668,7 +1666,6 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     const int chunks = (max_query_len + tpc - 1) / tpc;
     for (int c = 0; c < chunks; ++c) {
         a.chunk = c;
-        a.tag = next_tag();
         if (dispatch_dtype<kModeMulti>(a, plan, cache, sm) != hipSuccess) return PA_ERR_HIP;
     }
     return PA_OK;
@@ -1679,7 +1676,12 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
 extern "C" {
 
 const char* pa_status_string(pa_status_t status) {
-    switch (status) {
+    // A caller may pass any integer; read its bits rather than the enum, whose
+    // out-of-range values C++ leaves undefined.
+    int32_t code = 0;
+    static_assert(sizeof(status) == sizeof(code), "pa_status_t is an int");
+    std::memcpy(&code, &status, sizeof(code));
+    switch (code) {
         case PA_OK:
             return "ok";
         case PA_ERR_INVALID_ARG:
@@ -1697,6 +1699,8 @@ const char* pa_status_string(pa_status_t status) {
 }
 
 int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+size_t pa_workspace_sync_bytes(void) { return PA_WORKSPACE_SYNC_BYTES; }
 
 pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slot_mapping, void* k_cache,
                         void* v_cache, int32_t num_tokens, const pa_cache_desc_t* cache, pa_stream_t stream) {
@@ -1753,17 +1757,17 @@ pa_status_t pa_decode_ex(const void* q, const void* k_cache, const void* v_cache
                          int32_t max_blocks_per_seq, const pa_cache_desc_t* cache, void* workspace,
                          size_t workspace_bytes, int32_t num_workers, pa_stream_t stream) {
     return decode_impl(q, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_tables,
-                       context_lens, nullptr, 1, scale, 0.f, out, num_seqs, num_q_heads, max_blocks_per_seq,
-                       cache, workspace, workspace_bytes, num_workers, kModeDecode, stream);
+                       context_lens, nullptr, 1, num_seqs, scale, 0.f, out, num_seqs, num_q_heads,
+                       max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers, kModeDecode, stream);
 }
 
 pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
                       int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq, int32_t max_query_len,
-                      const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes, int32_t num_workers,
-                      pa_stream_t stream) {
+                      int32_t num_q_rows, const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
+                      int32_t num_workers, pa_stream_t stream) {
     return decode_impl(q, nullptr, nullptr, const_cast<void*>(k_cache), const_cast<void*>(v_cache), block_tables,
-                       context_lens, query_start, max_query_len, scale, 0.f, out, num_seqs, num_q_heads,
+                       context_lens, query_start, max_query_len, num_q_rows, scale, 0.f, out, num_seqs, num_q_heads,
                        max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers, kModeMulti, stream);
 }
 
@@ -1772,9 +1776,9 @@ pa_status_t pa_decode_append(const void* q, const void* k_new, const void* v_new
                              int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                              const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
                              int32_t num_workers, pa_stream_t stream) {
-    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, scale, 0.f, out,
-                       num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes, num_workers,
-                       kModeAppend, stream);
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, num_seqs, scale,
+                       0.f, out, num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes,
+                       num_workers, kModeAppend, stream);
 }
 
 pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -1784,9 +1788,9 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
                                   size_t workspace_bytes, int32_t num_workers, pa_stream_t stream) {
     if (rope_theta == 0.f) return PA_ERR_INVALID_ARG;  // 0 means "no rotation" inside
     if (cache && cache->dtype == PA_F32) return PA_ERR_UNSUPPORTED;  // f32: pa_rope, then pa_decode_append
-    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, scale, rope_theta,
-                       out, num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace, workspace_bytes,
-                       num_workers, kModeAppendRope, stream);
+    return decode_impl(q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, nullptr, 1, num_seqs, scale,
+                       rope_theta, out, num_seqs, num_q_heads, max_blocks_per_seq, cache, workspace,
+                       workspace_bytes, num_workers, kModeAppendRope, stream);
 }
 
 pa_status_t pa_rope(void* q, void* k, const int32_t* positions, int32_t num_tokens, int32_t num_q_heads,

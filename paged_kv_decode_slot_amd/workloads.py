@@ -327,6 +327,16 @@ def config_case(n: int) -> Case:
     return make_case(seed=n, **cfg)
 
 
+def twin_case(n: int, dtype: str = "f32") -> Case:
+    """Workload ``n`` drawn again with another storage dtype: the same seed, so the
+    same lengths, block tables and placement, and the same float32 draws, here
+    rounded into ``dtype`` (not rounded at all for f32)."""
+    cfg = dict(CONFIGS[n])
+    cfg["name"] = f"{cfg['name']} ({dtype} twin)"
+    cfg["dtype"] = dtype
+    return make_case(seed=n, **cfg)
+
+
 def decode_bytes(case: Case) -> int:
     """Bytes a decode step must move: every used K and V row, q, out, the used
     block-table entries and the context lengths."""
@@ -335,6 +345,13 @@ def decode_bytes(case: Case) -> int:
     qo = 2 * case.S * case.Hq * case.D * case.elt
     bt = 4 * int(((ctx + case.B - 1) // case.B).sum())
     return kv + qo + bt + 4 * case.S
+
+
+def kv_read_bytes(case: Case) -> int:
+    """K and V bytes a fused step reads from the pools: every cached position's rows
+    except the new token's, which come from k_new / v_new."""
+    ctx = case.context_lens.astype(np.int64)
+    return int(np.maximum(ctx - 1, 0).sum()) * case.Hkv * case.D * case.elt * 2
 
 
 def step_bytes(case: Case) -> int:

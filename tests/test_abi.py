@@ -11,6 +11,7 @@ from paged_kv_decode_slot_amd.binding import CacheDesc, EXPORTS
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = range(5)
+SYNC = 256 * 1024  # PA_WORKSPACE_SYNC_BYTES
 
 
 def header_functions():
@@ -35,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = pa.lib()
-    assert L.pa_abi_version() == 2
+    assert L.pa_abi_version() == 3
     for st in range(6):
         assert L.pa_status_string(st) != b"unknown status"
     assert L.pa_status_string(99) == b"unknown status"
@@ -117,19 +118,20 @@ def test_decode_append_rejects(kw, status):
     assert _append(_desc(), **kw) == status
 
 
-def _attend_call(desc, *, qs=A, maxq=4, **kw):
+def _attend_call(desc, *, qs=A, maxq=4, rows=8, **kw):
     base = dict(q=A, kc=A, vc=A, bt=A, ctx=A, out=A, S=2, Hq=4, maxblk=3, ws=A, ws_bytes=1 << 30, workers=64,
                 scale=0.125)
     base.update(kw)
     b = base
     return pa.lib().pa_attend(b["q"], b["kc"], b["vc"], b["bt"], b["ctx"], qs, b["scale"], b["out"], b["S"], b["Hq"],
-                              b["maxblk"], maxq, ctypes.byref(desc), b["ws"], b["ws_bytes"], b["workers"], None)
+                              b["maxblk"], maxq, rows, ctypes.byref(desc), b["ws"], b["ws_bytes"], b["workers"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(qs=None), INVALID), (dict(qs=A + 2), INVALID), (dict(maxq=-1), INVALID), (dict(q=None), INVALID),
     (dict(Hq=3), INVALID), (dict(Hq=34), UNSUPPORTED), (dict(ws=None), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
-    (dict(maxq=0, qs=None, q=None, out=None), OK), (dict(S=0, qs=None), OK),
+    (dict(maxq=0, qs=None, q=None, out=None), OK), (dict(S=0, qs=None), OK), (dict(rows=-1), INVALID),
+    (dict(rows=0, qs=None, q=None, out=None), OK),
 ])
 def test_attend_rejects(kw, status):
     assert _attend_call(_desc(), **kw) == status
@@ -143,7 +145,7 @@ def test_attend_workspace_sizes():
     r = lambda x: (x + 255) // 256 * 256
     for Hq, cols in [(32, 16), (56, 14), (8, 16), (128, 16)]:  # G = 4, 7, 1, 16: floor(16/G) tokens x G heads
         got = L.pa_attend_workspace_bytes(S, Hq, 256, ctypes.byref(d), W_)
-        assert got == r(8 * S * Hkv) + r(4 * waves * 2 * cols) + 4 * waves * 2 * cols * D
+        assert got == SYNC + r(4 * waves * 2 * cols) + 4 * waves * 2 * cols * D
     assert L.pa_attend_workspace_bytes(S, 32, 256, ctypes.byref(d), -1) == 0
 
 
@@ -177,18 +179,34 @@ def test_workspace_sizes():
     d = _desc(head_dim=128, num_kv_heads=8)
     # one worker per (sequence, kv-head slice): no workspace
     assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), -1) == 0
-    # stream split: an 8-byte arrival word per (sequence, kv-head), then
-    # 2 parts per wave of G lse values and G*D outputs; a worker has a wave
-    # per kv-head of its slice (the largest divisor of Hkv up to 2)
+    # stream split: the fixed synchronisation words, then 2 parts per wave of
+    # G lse values and G*D outputs; a worker has a wave per kv-head of its
+    # slice (the largest divisor of Hkv up to 2)
     r = lambda x: (x + 255) // 256 * 256
     for Hkv, Hq, sl in [(8, 32, 2), (4, 28, 2), (6, 24, 2), (16, 32, 2), (2, 4, 2), (7, 14, 1), (3, 3, 1), (1, 16, 1)]:
         d = _desc(head_dim=128, num_kv_heads=Hkv)
         W, S, G, D = 100, 64, Hq // Hkv, 128
         got = L.pa_decode_workspace_bytes_ex(S, Hq, 256, ctypes.byref(d), W)
-        assert got == r(8 * S * Hkv) + r(4 * W * sl * 2 * G) + 4 * W * sl * 2 * G * D, (Hkv, Hq)
+        assert got == SYNC + r(4 * W * sl * 2 * G) + 4 * W * sl * 2 * G * D, (Hkv, Hq)
     d = _desc(head_dim=128, num_kv_heads=8)
     # rejected shapes report 0
     assert L.pa_decode_workspace_bytes_ex(64, 33, 256, ctypes.byref(d), W) == 0
+
+
+def test_sync_region_size_matches_the_header():
+    text = open(os.path.join(ROOT, "include", "pagedattn.h")).read()
+    m = re.search(r"#define PA_WORKSPACE_SYNC_BYTES \((\d+) \* (\d+)\)", text)
+    assert m and int(m.group(1)) * int(m.group(2)) == SYNC == 256 * 1024
+
+
+def test_worker_count_bounded_by_the_arrival_words():
+    # one arrival word per wave of every worker, after 8 header words
+    L = pa.lib()
+    d = _desc(head_dim=128, num_kv_heads=8)  # slices of 2 kv-heads: 2 waves per worker
+    most = (SYNC // 8 - 8) // 2
+    assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), most) > 0
+    assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), most + 1) == 0
+    assert _decode(_desc(num_kv_heads=2), workers=most + 1) == UNSUPPORTED  # rejected before any launch
 
 
 def test_binding_refuses_cpu_tensors():
@@ -291,3 +309,19 @@ def test_rmsnorm_rejects_bad_arguments():
     assert norm(out=A + 8) == bad
     assert norm(res=A + 4) == bad
     assert norm(rows=0, x=None, w=None, out=None) == pa.binding.PA_OK  # nothing to do: no launch
+
+
+def test_read_probe_rejects_bad_arguments():
+    L = pa.lib()
+
+    def probe(src=A, ids=None, n=4, tile=4096, sink=A, waves=8):
+        return L.pa_read_probe(src, ids, n, tile, sink, waves, None)
+    assert probe(n=-1) == INVALID
+    assert probe(tile=0) == INVALID
+    assert probe(tile=1000) == INVALID       # not whole 1 KB runs
+    assert probe(waves=6) == INVALID         # not whole workgroups of 4 waves
+    assert probe(waves=0) == INVALID
+    assert probe(sink=None) == INVALID
+    assert probe(sink=A + 8) == INVALID
+    assert probe(src=A + 4) == INVALID
+    assert probe(ids=A + 2) == INVALID

@@ -116,3 +116,27 @@ def test_attend_no_query_tokens_is_a_noop():
     out = pa.attend(q, g.k_cache, g.v_cache, g.bt, g.ctx, qs, 0, case.scale)
     torch.cuda.synchronize()
     assert out.shape == (0, case.Hq, case.D)
+
+
+def test_attend_query_start_is_clamped_to_the_rows():
+    """query_start values outside [0, num_q_rows] are clamped: a first entry
+    below 0 and a last entry past the rows give exactly the answer of the
+    well-formed call, and rows past num_q_rows (guard rows here) stay untouched."""
+    case = W.make_case(S=5, Hq=8, Hkv=2, D=128, B=16, dtype="bf16", ctx_range=(40, 300), seed=631, name="clamp")
+    mc = W.with_queries(case, [3, 1, 7, 2, 5], seed=632)
+    g = _gpu(case)
+    R = int(mc.query_start[-1])
+    qs = torch.from_numpy(mc.query_start).to(DEV)
+    good = pa.attend(mc.q.to(DEV), g.k_cache, g.v_cache, g.bt, g.ctx, qs, mc.max_q_len, case.scale)
+    bad = mc.query_start.copy()
+    bad[0], bad[-1] = -4, R + 5
+    log(f"[attend] clamped query_start {bad.tolist()} over {R} rows")
+    q_full = torch.empty((R + 2, case.Hq, case.D), dtype=torch.bfloat16, device=DEV)
+    q_full[:R] = mc.q.to(DEV)
+    q_full[R:] = float("nan")
+    out_full = torch.full((R + 2, case.Hq, case.D), 7.0, dtype=torch.bfloat16, device=DEV)
+    pa.attend(q_full[:R], g.k_cache, g.v_cache, g.bt, g.ctx, torch.from_numpy(bad).to(DEV), mc.max_q_len,
+              case.scale, out=out_full[:R])
+    torch.cuda.synchronize()
+    assert torch.equal(dev_bits(out_full[:R]), dev_bits(good))
+    assert bool((out_full[R:] == 7.0).all())
