@@ -147,6 +147,27 @@ pa_status_t pa_decode(const void* q, const void* k_cache, const void* v_cache, c
                       size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * pa_decode for callers that cannot allocate device memory -- code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * allocation: the same computation with the same automatic split (bitwise
+ * the same output as pa_decode), with its workspace taken from a device
+ * array of PA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it
+ * runs on until the process ends.  It calls no allocator.  The first call on
+ * a device looks up that array's address and clears its synchronisation
+ * words with a small kernel on `stream`.
+ * All calls on one GPU share the one array: calls that overlap in time on a
+ * GPU (other streams, other host threads) race and give undefined results;
+ * issue them on one stream.  A plan larger than the array (not reached on
+ * MI355X: at most 2 wavefronts per compute unit, G <= 16, head_dim <= 128)
+ * returns PA_ERR_WORKSPACE.  Arguments as in pa_decode.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+pa_status_t pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t max_blocks_per_seq, const pa_cache_desc_t* cache,
+                              pa_stream_t stream);
+
+/*
  * Workspace bytes pa_decode needs for these shapes on the current device
  * (0 means none).  Returns 0 as well for arguments pa_decode would reject.
  */

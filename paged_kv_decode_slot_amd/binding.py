@@ -23,6 +23,7 @@ _ELT = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
 EXPORTS = (
     "pa_write_kv",
     "pa_decode",
+    "pa_decode_noalloc",
     "pa_decode_ex",
     "pa_decode_append",
     "pa_attend",
@@ -100,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.pa_write_kv.restype = ctypes.c_int
         L.pa_decode.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, P]
         L.pa_decode.restype = ctypes.c_int
+        L.pa_decode_noalloc.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P]
+        L.pa_decode_noalloc.restype = ctypes.c_int
         L.pa_decode_ex.argtypes = [P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, I32, P]
         L.pa_decode_ex.restype = ctypes.c_int
         L.pa_decode_append.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, I32, I32, I32, DP, P, SZ, I32, P]

@@ -42,6 +42,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "pagedattn.h"
@@ -1671,6 +1672,50 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     return PA_OK;
 }
 
+// ---------------------------------------------------------------- the allocation-free decode
+
+// The workspace of pa_decode_noalloc: a device array of the library's own, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in); it uses the
+// device address hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint4* p, int n) {
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// This device's copy of `scratch`, set up on the first call on the device:
+// its address, and its synchronisation words cleared by a small kernel on the
+// caller's stream (a kernel rather than a memset node, in case the call is
+// being captured into a graph).
+pa_status_t noalloc_scratch(hipStream_t stream, uint8_t** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+    uint8_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+        if (p == nullptr) {
+            void* ptr = nullptr;
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return PA_ERR_HIP;
+            const int words = PA_WORKSPACE_SYNC_BYTES / 16;
+            void* args[] = {&ptr, const_cast<int*>(&words)};
+            if (hipLaunchKernel(reinterpret_cast<const void*>(&zero_words_kernel), dim3(words / 256), dim3(256), args,
+                                0, stream) != hipSuccess)
+                return PA_ERR_HIP;
+            p = static_cast<uint8_t*>(ptr);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1825,6 +1870,23 @@ pa_status_t pa_decode(const void* q, const void* k_cache, const void* v_cache, c
                       size_t workspace_bytes, pa_stream_t stream) {
     return pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
                         max_blocks_per_seq, cache, workspace, workspace_bytes, 0, stream);
+}
+
+pa_status_t pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, float scale, void* out, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t max_blocks_per_seq, const pa_cache_desc_t* cache,
+                              pa_stream_t stream) {
+    // The plan pa_decode would take; 0 for arguments it rejects (pa_decode_ex then
+    // reports why) or when no split needs a workspace.
+    const size_t need = pa_decode_workspace_bytes(num_seqs, num_q_heads, max_blocks_per_seq, cache);
+    if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_WORKSPACE;
+    uint8_t* ws = nullptr;
+    if (need > 0 && num_seqs > 0) {
+        const pa_status_t st = noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+        if (st != PA_OK) return st;
+    }
+    return pa_decode_ex(q, k_cache, v_cache, block_tables, context_lens, scale, out, num_seqs, num_q_heads,
+                        max_blocks_per_seq, cache, ws, ws ? (size_t)PA_NOALLOC_SCRATCH_BYTES : 0, 0, stream);
 }
 
 }  // extern "C"

@@ -325,3 +325,16 @@ def test_read_probe_rejects_bad_arguments():
     assert probe(sink=A + 8) == INVALID
     assert probe(src=A + 4) == INVALID
     assert probe(ids=A + 2) == INVALID
+
+
+def test_decode_noalloc_rejects_before_any_launch():
+    L = pa.lib()
+
+    def call(q=A, S=2, Hq=4, desc=None):
+        d = desc or _desc()
+        return L.pa_decode_noalloc(q, A, A, A, A, ctypes.c_float(0.125), A, S, Hq, 3, ctypes.byref(d), None)
+    assert call(Hq=3) == INVALID
+    assert call(Hq=34) == UNSUPPORTED
+    assert call(q=None) == INVALID
+    assert call(desc=_desc(head_dim=96)) == UNSUPPORTED
+    assert call(S=0) == OK
