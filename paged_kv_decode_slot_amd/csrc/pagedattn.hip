@@ -369,6 +369,13 @@ __device__ inline void coherent_store(float* p, float v) {
 constexpr int kWaitVmcnt0 = 0x0F70;
 __device__ inline void wait_vmem_done() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); }
 __device__ inline void wait_stores_done() { wait_vmem_done(); }
+// Vector-memory operations complete in the order they were issued: wait until
+// at most N (< 64) of this wave's are still outstanding.
+template <int N>
+__device__ inline void wait_vmem_upto() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Count this wave's part of a split (sequence, kv-head); true for the wave
 // that stores the last part.  The word counts the parts stored so far: it is
@@ -391,6 +398,9 @@ typedef const int32_t __attribute__((address_space(4)))* ScalarPtr;
 
 #ifndef PA_TILE_BUFFERS
 #define PA_TILE_BUFFERS 2  // 16-token tiles in registers: one being consumed, the rest in flight
+#endif
+#ifndef PA_PREFETCH_RUNS
+#define PA_PREFETCH_RUNS 1  // a run loads the next run's first tile and Q while it consumes its last tile
 #endif
 #ifndef PA_KV_NONTEMPORAL
 #define PA_KV_NONTEMPORAL 1  // K/V are read once: hint the caches not to keep them
@@ -569,6 +579,10 @@ __device__ __attribute__((always_inline)) inline void rope_rows_lds(uint4* piece
     }
     __builtin_amdgcn_wave_barrier();
 }
+
+// Vector loads of a prefetched run start: its first tile (K and V pieces) and its Q pieces.
+template <int DT, int D>
+constexpr int kPrefetchLoads = 2 * Cfg<DT, D, 16>::kKFrag + Cfg<DT, D, 16>::kVPiece;
 
 template <int DT, int D, int B>
 struct Tile {
@@ -810,19 +824,92 @@ __device__ __attribute__((always_inline)) void merge_parts(const DecodeArgs& a, 
             merge_body<DT, D, 4, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, hs, wi, u0, L);
 }
 
-// Attend query group (s, kvh) over logical blocks [j0, j1) of sequence s, whose
-// (sequence, slice) occupies units [F, F + nb) of the split over W workers.
-// A run over the whole context writes out; otherwise the run stores a partial
-// in slot `slot` of wave wid (wave wi of its worker, which has hs waves), and
-// the wave that stores the pair's last partial merges them.  With several
-// query tokens (MODE kModeMulti) the pair's columns are its `rows` query
-// tokens (from query row row0) times the G heads, and column (i, h) sees
-// positions up to ctx - rows + i; otherwise the columns are the G heads of
-// sequence s's one token, which sees positions up to ctx - 1.
-template <int DT, int D, int B, int MODE>
-__device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, int s, int kvh, int ctx, int row0, int rows, int j0, int j1, int nb,
-                           int64_t F, int64_t Fv, int64_t U, int64_t W, int wid, int slot, int hs, int wi,
-                           MergeLds& mlds, const double* rw) {
+// One run of a worker: logical blocks [j0, j1) of pair (s, kvh), whose
+// (sequence, slice) occupies units [Fv, F + nb) of the split (the units before
+// F hold no block).  Every field is the same in all lanes of the wave.
+struct Run {
+    int s, kvh, ctx, row0, rows, j0, j1, nb, slot;
+    int64_t F, Fv;
+};
+
+// What a run starts from when it was prefetched: its first tile, its Q
+// pieces, the id of its first block (checked) and that of its second (raw),
+// all loaded while the run before it consumed its last tile.
+template <int DT, int D, int B>
+struct Prefetch {
+    Tile<DT, D, B> tile;
+    uint4 q[Cfg<DT, D, B>::kKFrag];
+    int phys;
+    int next_id;
+};
+
+// Q of the lane's column, in the B-operand form of the QK product.  Columns
+// n >= active are padding: they take column 0's row, so they only repeat its
+// scores (and its rescale decisions) and are never stored.  Every lane loads,
+// so the load is not under a lane mask.
+template <int DT, int D, bool MQ>
+__device__ inline void load_q(const DecodeArgs& a, const Run& r, uint4* qf) {
+    constexpr int E = DT == PA_F32 ? 4 : 2;
+    const int lane = threadIdx.x & 63, n = lane & 15, rg = lane >> 4;
+    const int active = MQ ? r.rows * a.group : a.group;
+    const int qc = n < active ? n : 0;
+    const uint8_t* qrow = a.q + col_offset<MQ>(a, r.s, r.kvh, r.row0, qc, D) * E;
+#pragma unroll
+    for (int f = 0; f < Cfg<DT, D, 16>::kKFrag; ++f) qf[f] = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * rg);
+}
+
+// The loads of tile `tau` of a run whose current block id is `phys`: the
+// 16-token slab tau % kSub of (block, kv-head), 16 * D contiguous elements of
+// either pool.
+template <int DT, int D, int B>
+__device__ inline void load_tile(const DecodeArgs& a, int phys, int kvh, int u, Tile<DT, D, B>& t) {
+    using C = Cfg<DT, D, B>;
+    const int lane = threadIdx.x & 63, n = lane & 15, r = lane >> 4;
+    const size_t slab = (size_t)phys * a.num_kv_heads * C::kTileBytes + (size_t)kvh * C::kTileBytes +
+                        (size_t)u * C::kSlabBytes;
+    const uint8_t* kt = a.k_cache + slab;
+    const uint8_t* vt = a.v_cache + slab;
+#pragma unroll
+    for (int f = 0; f < C::kKFrag; ++f)
+        t.k[f] = __builtin_bit_cast(uint4, load_kv<u32x4>(kt + ((4 * f + r) * 16 + n) * 16));
+#pragma unroll
+    for (int c = 0; c < C::kVPiece; ++c)
+        t.v[c] = __builtin_bit_cast(uint4, load_kv<u32x4>(vt + ((r * C::kVPiece + c) * 16 + n) * 16));
+}
+
+// Start run r early: its first block id (already read: id0) and the one after,
+// its first tile and its Q.
+template <int DT, int D, int B, bool MQ>
+__device__ __attribute__((always_inline)) inline void prefetch_run(const DecodeArgs& a, const Run& r, int id0,
+                                                                   Prefetch<DT, D, B>& pf) {
+    const ScalarPtr bt = (ScalarPtr)(a.block_tables + (size_t)r.s * a.max_blocks);
+    pf.phys = ((unsigned)id0 < (unsigned)a.num_blocks) ? id0 : 0;
+    // (read unconditionally: j0 + 1 is inside the row unless j0 is its last entry,
+    // and then the value is never used)
+    pf.next_id = bt[r.j0 + 1 < a.max_blocks ? r.j0 + 1 : r.j0];
+    load_tile<DT, D, B>(a, pf.phys, r.kvh, 0, pf.tile);
+    load_q<DT, D, MQ>(a, r, pf.q);
+}
+
+// Attend pair (s, kvh) of run r over its blocks [j0, j1).  A run over the
+// whole context writes out; otherwise the run stores a partial in slot
+// r.slot of wave wid (wave wi of its worker, which has hs waves), and the wave
+// that stores the pair's last partial merges them.  With several query tokens
+// (MODE kModeMulti) the pair's columns are its `rows` query tokens (from query
+// row row0) times the G heads, and column (i, h) sees positions up to
+// ctx - rows + i; otherwise the columns are the G heads of sequence s's one
+// token, which sees positions up to ctx - 1.
+// With PF, the run's first tile and Q are already in flight in pf, and when
+// `more` is set the run loads the next run's (nx) into pf while it consumes
+// its own last tile, so that the next run never waits a full memory latency
+// for its first tile.
+template <int DT, int D, int B, int MODE, bool PF>
+__device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, const Run& rn, bool more, const Run& nx,
+                                                          Prefetch<DT, D, B>& pf, int64_t U, int64_t W, int wid,
+                                                          int hs, int wi, MergeLds& mlds, const double* rw) {
+    const int s = rn.s, kvh = rn.kvh, ctx = rn.ctx, row0 = rn.row0, rows = rn.rows, j0 = rn.j0, j1 = rn.j1,
+              nb = rn.nb, slot = rn.slot;
+    const int64_t F = rn.F, Fv = rn.Fv;
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
     constexpr int NBUF = PA_TILE_BUFFERS;
@@ -841,17 +928,20 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
     // the whole wave), one block ahead, so waiting for one never waits on the
     // K/V loads in flight.
     const ScalarPtr bt = (ScalarPtr)(a.block_tables + (size_t)s * a.max_blocks);
-    int next_id = bt[j0];
+    int next_id = PF ? pf.next_id : bt[j0];
+    // The next run's first block id, read now so that it is at hand when this
+    // run issues the next run's first tile.
+    int nx_id0 = 0;
+    if constexpr (PF) {
+        if (more) nx_id0 = ((ScalarPtr)(a.block_tables + (size_t)nx.s * a.max_blocks))[nx.j0];
+    }
 
-    // Q of the lane's column, in the B-operand form of the QK product.  Columns
-    // n >= active are padding: they take column 0's row, so they only repeat
-    // its scores (and its rescale decisions) and are never stored.  Every lane
-    // loads, so the load is not under a lane mask.
     uint4 qf[C::kKFrag];
-    {
-        const uint8_t* qrow = a.q + col_offset<MQ>(a, s, kvh, row0, qc, D) * E;
+    if constexpr (PF) {
 #pragma unroll
-        for (int f = 0; f < C::kKFrag; ++f) qf[f] = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * r);
+        for (int f = 0; f < C::kKFrag; ++f) qf[f] = pf.q[f];
+    } else {
+        load_q<DT, D, MQ>(a, rn, qf);
     }
 
     f32x4 O[C::kVChunk];
@@ -860,8 +950,6 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
     float m = -INFINITY;  // running max (log2 domain) of this lane's head
     float lsum = 0.f;     // this lane's share of the running denominator
 
-    const size_t blk_stride = (size_t)a.num_kv_heads * C::kTileBytes;
-    const size_t head_off = (size_t)kvh * C::kTileBytes;
     const int ntiles = (j1 - j0) * C::kSub;
 
     // Fused append: the run that holds the sequence's last block owns the new
@@ -896,23 +984,29 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
         }
     }
 
-    int phys = 0;
+    int phys = PF ? pf.phys : 0;
     auto issue = [&](int tau, Tile<DT, D, B>& t) {
         const int j = j0 + tau / C::kSub, u = tau % C::kSub;
         if (u == 0) {  // first tile of block j: take its id, fetch the next one
             phys = ((unsigned)next_id < (unsigned)a.num_blocks) ? next_id : 0;
             if (j + 1 < j1) next_id = bt[j + 1];
         }
-        // The 16-token slab u of this (block, kv-head) tile: 16 * D contiguous elements.
-        const size_t slab = (size_t)phys * blk_stride + head_off + (size_t)u * C::kSlabBytes;
-        const uint8_t* kt = a.k_cache + slab;
-        const uint8_t* vt = a.v_cache + slab;
+        load_tile<DT, D, B>(a, phys, kvh, u, t);
+    };
+    // The next run's first tile and Q, in place of the tile after this run's last.
+    // (With no next run pf is cleared instead, so that on every path its old
+    // contents -- this run's first tile and Q -- are dead once copied out.)
+    auto prefetch_next = [&]() {
+        if constexpr (PF) {
+            if (more) {
+                prefetch_run<DT, D, B, MQ>(a, nx, nx_id0, pf);
+            } else {
 #pragma unroll
-        for (int f = 0; f < C::kKFrag; ++f)
-            t.k[f] = __builtin_bit_cast(uint4, load_kv<u32x4>(kt + ((4 * f + r) * 16 + n) * 16));
+                for (int f = 0; f < C::kKFrag; ++f) pf.tile.k[f] = pf.q[f] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int c = 0; c < C::kVPiece; ++c)
-            t.v[c] = __builtin_bit_cast(uint4, load_kv<u32x4>(vt + ((r * C::kVPiece + c) * 16 + n) * 16));
+                for (int c = 0; c < C::kVPiece; ++c) pf.tile.v[c] = make_uint4(0, 0, 0, 0);
+            }
+        }
     };
 
     // m is a reference maximum, not necessarily the running one: weights are
@@ -994,17 +1088,27 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
         }
     };
     Tile<DT, D, B> buf[NBUF];
+    // The run's first tile: already in flight when it was prefetched.
+    auto first = [&]() {
+        if constexpr (PF)
+            buf[0] = pf.tile;
+        else
+            issue(0, buf[0]);
+    };
     if (ntiles < NBUF) {
+        first();
 #pragma unroll
-        for (int i = 0; i < NBUF; ++i)
+        for (int i = 1; i < NBUF; ++i)
             if (i < ntiles) issue(i, buf[i]);
+        prefetch_next();
         rotate_inputs();
 #pragma unroll
         for (int i = 0; i < NBUF; ++i)
             if (i < ntiles) consume(i, buf[i], true);
     } else {
+        first();
 #pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i) issue(i, buf[i]);
+        for (int i = 1; i < NBUF - 1; ++i) issue(i, buf[i]);
         rotate_inputs();
         int tau0 = 0;
         for (; tau0 + NBUF - 1 + kTail < ntiles; tau0 += NBUF) {
@@ -1018,16 +1122,20 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, i
         for (int k = 0; k < NBUF + kTail; ++k) {
             const int tau = tau0 + k;
             if (tau < ntiles) {
-                if (tau + NBUF - 1 < ntiles) issue(tau + NBUF - 1, buf[(k + NBUF - 1) % NBUF]);
+                if (tau + NBUF - 1 < ntiles)
+                    issue(tau + NBUF - 1, buf[(k + NBUF - 1) % NBUF]);
+                else if (tau + NBUF - 1 == ntiles)
+                    prefetch_next();
                 consume(tau, buf[k % NBUF], true);
             }
         }
     }
 
-    // Every tile load has been consumed; saying so before the stores below keeps
-    // the compiler from draining the next run's first loads for a load it
-    // cannot prove done (a register it would overwrite).
-    wait_vmem_done();
+    // Every tile load of this run has been consumed; only the next run's
+    // prefetch (issued last) may still be in flight.  Saying so before the
+    // stores below keeps the compiler from draining loads for a register it
+    // cannot prove written.
+    wait_vmem_upto<PF ? kPrefetchLoads<DT, D> : 0>();
 
     // Full denominator of the lane's head: the four row groups hold disjoint tokens.
     lsum = row_group_sum(lsum);
@@ -1253,7 +1361,11 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         start = (int64_t)g * U / W;
         end = (int64_t)(g + 1) * U / W;
     }
-    for (int64_t u = start; u < end;) {
+    // The worker's runs in unit order, one at a time; a range that ends inside
+    // a pair's leading units holds no block and is skipped.
+    int64_t u = start;
+    auto next_run = [&](Run& run) -> bool {
+      while (u < end) {
         // Every lane holds the same values; readfirstlane lets them live in scalar registers.
         const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, (int)(u / hc)));
         const int base = __builtin_amdgcn_readfirstlane(s_pre[s]);
@@ -1270,10 +1382,34 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
         const int64_t Fv = (int64_t)base * hc + (int64_t)c * nbv;  // the (sequence, slice)'s first unit
         const int row0 = MQ ? __builtin_amdgcn_readfirstlane(s_row0[s]) : 0;
         const int rows = MQ ? __builtin_amdgcn_readfirstlane(s_rows[s]) : 1;
-        if (j1 > j0)  // a range that ends inside the leading units holds no block
-            attend_run<DT, D, B, MODE>(a, s, kvh, ctx, row0, rows, j0, j1, nb, Fv + cost, Fv, U, W, wid,
-                                       u == start ? 0 : 1, hs, wi, s_merge[wi], s_rope_w);
+        const int slot = u == start ? 0 : 1;
         u += jv1 - jv0;
+        if (j1 > j0) {
+            run = Run{s, kvh, ctx, row0, rows, j0, j1, nb, slot, Fv + cost, Fv};
+            return true;
+        }
+      }
+      return false;
+    };
+    // Each run after the first starts from what the run before it prefetched.
+    // (Measured: 1.7 us off the ragged 256-sequence decode, none elsewhere; with
+    // the append's registers on top it made the fused step slower, so only the
+    // plain decode does it.)
+    constexpr bool PF = PA_PREFETCH_RUNS && MODE == kModeDecode;
+    Prefetch<DT, D, B> pf;
+    Run cur{};
+    bool have = next_run(cur);
+    if constexpr (PF) {
+        if (have)
+            prefetch_run<DT, D, B, MQ>(a, cur, ((ScalarPtr)(a.block_tables + (size_t)cur.s * a.max_blocks))[cur.j0],
+                                       pf);
+    }
+    while (have) {
+        Run nx{};
+        const bool more = next_run(nx);
+        attend_run<DT, D, B, MODE, PF>(a, cur, more, nx, pf, U, W, wid, hs, wi, s_merge[wi], s_rope_w);
+        cur = nx;
+        have = more;
     }
 }
 
