@@ -202,6 +202,59 @@ def measure_attend(n, q_len, args, device):
                 traffic=measured_traffic(n, f"attend{q_len}"))
 
 
+def chunk_q_lens(case):
+    """The mixed batch of the chunk leg: every 8th sequence carries a prompt chunk
+    (64 to 512 tokens), the others one decode token each."""
+    import numpy as np
+
+    q_lens = np.ones(case.S, dtype=np.int64)
+    q_lens[::8] = [64, 96, 128, 200, 256, 300, 400, 512][:len(q_lens[::8])]
+    return q_lens
+
+
+def measure_chunks(n, args, device):
+    """pa_attend on workload n's pools with a mixed batch: prompt chunks of 64 to 512
+    tokens beside decode tokens, K calls back to back.  Reports query rows/s, the
+    chunk kernel's matrix-core rate (causal FLOPs of the chunk tokens) and the
+    bytes the call must read."""
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_slot_amd as pa
+    from paged_kv_decode_slot_amd import workloads as W
+
+    case = W.config_case(n)
+    mc = W.with_queries(case, chunk_q_lens(case), seed=2000 + n)
+    layer_bytes = 2 * case.pool_numel * case.elt
+    layers = args.layers or max(2, math.ceil(2 * 2**30 / layer_bytes))
+    steps, pools = setup_layers(case, layers, device, args.workers)
+    for (w, _d, _f) in steps:
+        w()
+    q = mc.q.to(device)
+    qs = torch.from_numpy(mc.query_start).to(device)
+    bt = torch.from_numpy(case.block_tables).to(device)
+    ctx = torch.from_numpy(case.context_lens).to(device)
+    out = torch.empty_like(q)
+    calls = [pa.prepare_attend(q, kc, vc, bt, ctx, qs, mc.max_q_len, case.scale, out, num_workers=args.workers)
+             for (kc, vc) in pools]
+    ms = time_back_to_back(calls, args.steps, args.warmup)
+    us = ms * 1e3 / args.steps
+    ql = mc.q_lens.astype(np.int64)
+    L = case.context_lens.astype(np.int64)
+    chunk = ql > 1
+    # causal FLOPs: token i of a sequence sees L - n + i + 1 positions; 4 flops per (position, head, dim)
+    seen = sum(int(((L[s] - ql[s]) * ql[s] + ql[s] * (ql[s] + 1) // 2)) for s in np.nonzero(chunk)[0])
+    flops = 4 * seen * case.Hq * case.D
+    b = W.attend_bytes(mc)
+    rows = int(mc.query_start[-1])
+    return dict(workload=W.CONFIGS[n]["name"], query_lens=f"{int(chunk.sum())} prompt chunks {ql[chunk].tolist()}, "
+                f"{int((~chunk).sum())} decode tokens", us=round(us, 2), query_rows=rows,
+                query_rows_per_s=round(rows / (us * 1e-6)), chunk_tflops=round(flops / (us * 1e-6) / 1e12, 1),
+                bytes=b, gbs=round(b / (us * 1e-6) / 1e9, 1),
+                note="one pa_attend call: chunk_kernel for the chunks, the split path for the decode tokens; "
+                     "chunk_tflops counts only the chunks' causal FLOPs over the whole call's time")
+
+
 def measure_rope(n, theta, args, device):
     """The decode step with the rotary embedding of q and the new K rows fused
     in (pa_decode_rope_append), beside pa_rope + pa_decode_append, K steps back
@@ -454,6 +507,7 @@ def main():
     ap.add_argument("--rope-theta", type=float, default=500000.0,
                     help="also time the step with the rotary embedding fused in, at this base (0: skip)")
     ap.add_argument("--no-pool", action="store_true", help="skip the block-pool leg")
+    ap.add_argument("--no-chunks", action="store_true", help="skip the prompt-chunk leg")
     ap.add_argument("--no-norm", action="store_true", help="skip the RMSNorm leg")
     ap.add_argument("--no-ceilings", action="store_true", help="skip the read-bandwidth ceilings")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -508,6 +562,11 @@ def main():
     attend = None
     if args.attend_q > 0:
         attend = measure_attend(args.config, args.attend_q, args, device)
+        torch.cuda.empty_cache()
+
+    chunks = None
+    if not args.no_chunks:
+        chunks = measure_chunks(args.config, args, device)
         torch.cuda.empty_cache()
 
     rope = None
@@ -590,6 +649,7 @@ def main():
                 "t_decode_us_per_launch_events": r2(main_res["t_decode_us_events"]),
             },
             "attend": attend,
+            "chunks": chunks,
             "rope": rope,
             "pool": pool,
             "rmsnorm": norm,

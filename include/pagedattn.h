@@ -268,9 +268,14 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
  *   num_q_rows     : host value, the rows of q and out
  *   other arguments as in pa_decode_ex; the workspace must hold
  *   pa_attend_workspace_bytes(...) bytes
- * Query tokens are taken floor(16 / G) at a time (one launch per group of
- * tokens, all on `stream`): a group reads the K/V its tokens see once, so
- * n > floor(16 / G) re-reads a sequence's K/V once per group.
+ * Two paths, chosen per sequence on the device.  A sequence with at most
+ * C = 4 x floor(16 / G) tokens (2 x for f32 with head_dim 128) takes the split
+ * path of pa_decode_ex: its tokens floor(16 / G) at a time (one launch per
+ * group, all on `stream`), each group a matrix-core tile that reads the K/V
+ * its tokens see once.  A longer one (a prompt chunk) is cut into blocks of C
+ * tokens, each attended by one workgroup whose four waves split the positions
+ * and merge at the end: its K/V is read once per block (from HBM about once
+ * in all, the blocks of a sequence running side by side).
  * Preconditions (unchecked): n <= L, and those of pa_decode.  A column whose
  * tokens see no position (only possible when n > L) gives 0.
  */
@@ -280,7 +285,8 @@ pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, c
                       int32_t num_q_rows, const pa_cache_desc_t* cache, void* workspace, size_t workspace_bytes,
                       int32_t num_workers, pa_stream_t stream);
 
-/* Workspace bytes pa_attend needs for these shapes and num_workers (0 for arguments it rejects). */
+/* Workspace bytes pa_attend needs for these shapes and num_workers (0 for arguments it rejects);
+ * at least PA_WORKSPACE_SYNC_BYTES, whose words also count the prompt-chunk work items. */
 size_t pa_attend_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                  const pa_cache_desc_t* cache, int32_t num_workers);
 

@@ -42,6 +42,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -252,6 +253,7 @@ struct DecodeArgs {
     int32_t num_q_rows;   // several query tokens: rows of q and out (query_start values are clamped to it)
     int32_t chunk;        // several query tokens: this launch takes tokens [chunk*tpc, (chunk+1)*tpc) of each
     int32_t tpc;          // several query tokens: tokens per pair (16 / G)
+    int32_t chunk_min;    // several query tokens: sequences with more tokens than this go to chunk_kernel
     double rope_w[kMaxRopePairs];  // append with rotary embedding: frequencies theta^(-2i/D), i < D/2
 };
 
@@ -306,7 +308,8 @@ __device__ __attribute__((always_inline)) void load_lengths(const DecodeArgs& a,
             const int q0 = min(max(a.query_start[i], 0), a.num_q_rows);
             const int n = min(max(a.query_start[i + 1], q0), a.num_q_rows) - q0;
             const int i0 = a.chunk * a.tpc;
-            const int nr = i0 < n ? min(a.tpc, n - i0) : 0;
+            // (a sequence with more than chunk_min tokens is chunk_kernel's)
+            const int nr = (i0 < n && n <= a.chunk_min) ? min(a.tpc, n - i0) : 0;
             c = nr > 0 ? max(0, min(c, c - n + i0 + nr)) : 0;
             row0[i] = q0 + i0;
             rows[i] = nr;
@@ -1413,6 +1416,286 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
     }
 }
 
+// ---------------------------------------------------------------- prompt chunks
+
+// Causal attention of many query tokens of a sequence at once (a prompt split
+// into chunks that run beside decode steps: ForgeLLM README, feature list and
+// the paragraph under its architecture flowchart).  A workgroup takes one
+// (sequence, kv-head, block of query tokens): NT matrix-core column tiles of
+// tpc tokens x G heads, so every K/V tile feeds NT QK and NT PV products.  Its
+// four waves hold the same columns and split the positions those tokens see
+// into four contiguous ranges of 16-token tiles, each read once, with the
+// online softmax of the split path per column; the four partial states are
+// merged through LDS at the end (the same log-sum-exp identity as the split
+// merge).  The grid is persistent, one workgroup per compute unit: each builds
+// the per-sequence prefix of item counts in LDS once and then takes items
+// from a counter in the workspace's synchronisation words (the last workgroup
+// to finish puts the counter back to zero).  Sequences with at most chunk_min
+// tokens are left to decode_kernel's several-token mode.
+constexpr int kChunkThreads = 256;
+constexpr int kChunkWaves = kChunkThreads / kWave;
+
+#ifndef PA_CHUNK_TILES
+#define PA_CHUNK_TILES 0  // 0: by row size
+#endif
+// Column tiles per workgroup: as many as registers hold beside the K/V tile ring.
+template <int DT, int D>
+constexpr int chunk_tiles() {
+    return PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (D * (DT == PA_F32 ? 4 : 2) <= 256 ? 4 : 2);
+}
+
+// Query rows of sequence i (query_start clamped into [0, num_q_rows]).
+__device__ inline void query_rows(const DecodeArgs& a, int i, int& q0, int& nq) {
+    q0 = min(max(a.query_start[i], 0), a.num_q_rows);
+    nq = min(max(a.query_start[i + 1], q0), a.num_q_rows) - q0;
+}
+
+// The attention of one item: sequence s, kv-head g, query block qb.
+template <int DT, int D, int B>
+__device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, int s, int g, int qb, f32x4 (*s_o)[Cfg<DT, D, B>::kVChunk][kWave],
+                                                          float (*s_m)[kWave], float (*s_l)[kWave]) {
+    using C = Cfg<DT, D, B>;
+    constexpr int E = C::kElt;
+    constexpr int NT = chunk_tiles<DT, D>();
+    constexpr float kLazy = 8.f;
+    const int lane = threadIdx.x & 63, n = lane & 15, r = lane >> 4;
+    const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int G = a.group, tpc = a.tpc;
+    const int QB = NT * tpc;  // query tokens of a workgroup
+    int q0, nq;
+    query_rows(a, s, q0, nq);
+    const int i_begin = qb * QB;  // the item's first token
+    const int L = clamp_ctx(a.context_lens[s], B, a.max_blocks);
+    const int ntok = min(QB, nq - i_begin);
+
+    // Per column tile: the lane's token (padding columns and tokens past the
+    // sequence's take the tile's first column, or the block's first token:
+    // same scores, never stored), the last position it sees, and its Q pieces.
+    const bool col_real = n < tpc * G;
+    int lim[NT];
+    uint4 qf[NT][C::kKFrag];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        const int first = min(i_begin + ct * tpc, nq - 1);
+        const int t = col_real ? first + n / G : first;
+        const bool ok = col_real && t < nq;
+        const int tk = ok ? t : first;
+        lim[ct] = L - nq + tk;
+        const int h = ok ? n % G : 0;
+        const uint8_t* qrow = a.q + ((size_t)(q0 + tk) * a.num_q_heads + g * G + h) * (size_t)(D * E);
+#pragma unroll
+        for (int f = 0; f < C::kKFrag; ++f) qf[ct][f] = *reinterpret_cast<const uint4*>(qrow + 64 * f + 16 * r);
+    }
+    // Positions the block's tokens see: tiles [0, T); this wave takes
+    // [tau_lo, tau_hi).  Tiles before tau_mask are seen whole by every column.
+    const int lim_last = L - nq + i_begin + ntok - 1;
+    const int lim_first = L - nq + i_begin;
+    const int T = lim_last >= 0 ? lim_last / 16 + 1 : 0;
+    const int tau_lo = wi * T / kChunkWaves, tau_hi = (wi + 1) * T / kChunkWaves;
+    const int tau_mask = lim_first >= 0 ? (lim_first + 1) / 16 : 0;
+    const int nblk = (T + C::kSub - 1) / C::kSub;
+
+    f32x4 O[NT][C::kVChunk];
+    float m[NT], lsum[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+#pragma unroll
+        for (int c = 0; c < C::kVChunk; ++c) O[ct][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[ct] = -INFINITY;
+        lsum[ct] = 0.f;
+    }
+
+    const ScalarPtr bt = (ScalarPtr)(a.block_tables + (size_t)s * a.max_blocks);
+    int next_id = tau_lo < tau_hi ? bt[tau_lo / C::kSub] : 0;
+    int phys = 0;
+    auto issue = [&](int tau, Tile<DT, D, B>& t) {
+        const int j = tau / C::kSub, u = tau % C::kSub;
+        if (u == 0 || tau == tau_lo) {
+            phys = ((unsigned)next_id < (unsigned)a.num_blocks) ? next_id : 0;
+            if (j + 1 < nblk) next_id = bt[j + 1];
+        }
+        load_tile<DT, D, B>(a, phys, g, u, t);
+    };
+    // One tile: all NT score tiles first (independent products the matrix core
+    // can overlap), then the softmax of every column with one rarely taken
+    // branch for the rescales, then all NT PV products.
+    auto consume = [&](int tau, Tile<DT, D, B>& t) {
+        const int tok0 = 16 * tau + 4 * r;  // position of this lane's first row
+        const bool partial = tau >= tau_mask;
+        f32x4 sc[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            sc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int f = 0; f < C::kKFrag; ++f) sc[ct] = qk_step<DT>(t.k[f], qf[ct][f], sc[ct]);
+        }
+        if (partial) {
+#pragma unroll
+            for (int c = 0; c < C::kVPiece; ++c) mask_v<E>(t.v[c], tok0, L);
+        }
+        float z[NT][4], tmax[NT];
+        bool up = false;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                z[ct][e] = sc[ct][e] * a.scale_log2;
+                if (partial && tok0 + e > lim[ct]) z[ct][e] = -INFINITY;
+            }
+            tmax[ct] = row_group_max(fmaxf(fmaxf(z[ct][0], z[ct][1]), fmaxf(z[ct][2], z[ct][3])));
+            up = up || tmax[ct] > m[ct] + kLazy;
+        }
+        if (__builtin_amdgcn_read_exec() & __ballot(up)) {
+#pragma unroll
+            for (int ct = 0; ct < NT; ++ct) {
+                const float m_new = fmaxf(m[ct], tmax[ct]);
+                if (m_new > m[ct] + kLazy) {
+                    const float alpha = __builtin_amdgcn_exp2f(m[ct] - m_new);  // 0 while m is -inf
+                    lsum[ct] *= alpha;
+#pragma unroll
+                    for (int c = 0; c < C::kVChunk; ++c) O[ct][c] *= alpha;
+                    m[ct] = m_new;
+                }
+            }
+        }
+        PPack<DT> pp[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+            float p[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] = (z[ct][e] > -INFINITY) ? __builtin_amdgcn_exp2f(z[ct][e] - m[ct]) : 0.f;
+            lsum[ct] += (p[0] + p[1]) + (p[2] + p[3]);
+            pp[ct] = pack_p<DT>(p);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+#pragma unroll
+            for (int c = 0; c < C::kVPiece; ++c) pv_piece<DT>(t.v[c], pp[ct], &O[ct][c * (4 / E)]);
+        }
+    };
+
+    // Two tiles in registers: the next one's loads are in flight while one is
+    // consumed.  Every step issues a load (the last tile again at the very
+    // end, unused), so no load sits under a branch.
+    Tile<DT, D, B> buf[2];
+    if (tau_lo < tau_hi) {
+        issue(tau_lo, buf[0]);
+        int tau = tau_lo;
+        for (; tau + 1 < tau_hi; tau += 2) {
+            issue(tau + 1, buf[1]);
+            consume(tau, buf[0]);
+            issue(min(tau + 2, tau_hi - 1), buf[0]);
+            consume(tau + 1, buf[1]);
+        }
+        if (tau < tau_hi) consume(tau, buf[0]);
+    }
+    wait_vmem_done();
+
+    // Merge the four waves' states, one column tile at a time: waves 1..3 put
+    // theirs in LDS, wave 0 combines them with its own and stores the output.
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+        if (wi > 0) {
+#pragma unroll
+            for (int c = 0; c < C::kVChunk; ++c) s_o[wi - 1][c][lane] = O[ct][c];
+            s_m[wi - 1][lane] = m[ct];
+            s_l[wi - 1][lane] = lsum[ct];
+        }
+        __syncthreads();
+        if (wi == 0) {
+            float M = m[ct];
+#pragma unroll
+            for (int w = 0; w < kChunkWaves - 1; ++w) M = fmaxf(M, s_m[w][lane]);
+            // (M is -inf only for a column that sees no position: nq > L)
+            const float a0 = M > -INFINITY ? __builtin_amdgcn_exp2f(m[ct] - M) : 0.f;
+            float l = lsum[ct] * a0;
+            f32x4 acc[C::kVChunk];
+#pragma unroll
+            for (int c = 0; c < C::kVChunk; ++c) acc[c] = O[ct][c] * a0;
+#pragma unroll
+            for (int w = 0; w < kChunkWaves - 1; ++w) {
+                const float aw = M > -INFINITY ? __builtin_amdgcn_exp2f(s_m[w][lane] - M) : 0.f;
+                l += s_l[w][lane] * aw;
+#pragma unroll
+                for (int c = 0; c < C::kVChunk; ++c) acc[c] += s_o[w][c][lane] * aw;
+            }
+            l = row_group_sum(l);
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            const int t = i_begin + ct * tpc + n / G;
+            if (col_real && t < nq) {
+                uint8_t* orow = a.out + ((size_t)(q0 + t) * a.num_q_heads + g * G + n % G) * (size_t)(D * E);
+#pragma unroll
+                for (int c = 0; c < C::kVChunk; ++c) store4<DT>(orow + (16 * c + 4 * r) * E, acc[c] * inv);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int DT, int D, int B>
+__global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(DecodeArgs a) {
+    using C = Cfg<DT, D, B>;
+    constexpr int NT = chunk_tiles<DT, D>();
+    // The merge area: waves 1..3 hand one column tile's state to wave 0 at a time.
+    __shared__ f32x4 s_o[kChunkWaves - 1][C::kVChunk][kWave];
+    __shared__ float s_m[kChunkWaves - 1][kWave], s_l[kChunkWaves - 1][kWave];
+    __shared__ int32_t s_wave_tot[kChunkWaves];
+    __shared__ int32_t s_item;
+    extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];  // [num_seqs + 1]: items before sequence s
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S = a.num_seqs, Hkv = a.num_kv_heads, QB = NT * a.tpc;
+    // Items of a sequence: its query blocks times the kv-heads, when it has
+    // more than chunk_min tokens.  Exclusive prefix over sequences into LDS.
+    auto items_of = [&](int i) {
+        int q0, nq;
+        query_rows(a, i, q0, nq);
+        return nq > a.chunk_min ? (nq + QB - 1) / QB * Hkv : 0;
+    };
+    const int per = (S + kChunkThreads - 1) / kChunkThreads;
+    const int lo = min(S, tid * per), hi = min(S, lo + per);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += items_of(i);
+    int x = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) s_wave_tot[wave] = x;
+    __syncthreads();
+    int run = x - sum;
+    for (int w = 0; w < wave; ++w) run += s_wave_tot[w];
+    for (int i = lo; i < hi; ++i) {
+        s_pre[i] = run;
+        run += items_of(i);
+    }
+    if (tid == kChunkThreads - 1) s_pre[S] = run;
+    __syncthreads();
+    const int nitems = s_pre[S];
+
+    // Items in order (sequence, kv-head, query block), taken from the counter.
+    unsigned long long* counter = a.sync;
+    for (;;) {
+        if (tid == 0) s_item = (int)atomicAdd(counter, 1ull);
+        __syncthreads();
+        const int item = __builtin_amdgcn_readfirstlane(s_item);
+        __syncthreads();
+        if (item >= nitems) break;
+        const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, item));
+        const int nqb = (s_pre[s + 1] - s_pre[s]) / Hkv;
+        const int local = item - s_pre[s];
+        chunk_item<DT, D, B>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
+    }
+    // The last workgroup out puts the counter (and its own count) back to zero.
+    if (tid == 0) {
+        if (atomicAdd(counter + 1, 1ull) + 1 == gridDim.x) {
+            atomicExch(counter, 0ull);
+            atomicExch(counter + 1, 0ull);
+        }
+    }
+}
+
 // ---------------------------------------------------------------- KV append
 
 struct WriteArgs {
@@ -1706,6 +1989,40 @@ int tokens_per_pair(int num_q_heads, const pa_cache_desc_t* cache) {
     return G >= 16 ? 1 : 16 / G;
 }
 
+// Tokens of one chunk_kernel wave (its column tiles x tpc): sequences with more
+// query tokens than this take chunk_kernel.
+int chunk_min_tokens(const pa_cache_desc_t* cache, int tpc) {
+    const int row_bytes = cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2);
+    return (PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (row_bytes <= 256 ? 4 : 2)) * tpc;
+}
+
+template <int DT, int D, int B>
+hipError_t launch_chunk(const DecodeArgs& a, int items, hipStream_t stream) {
+    static_assert(PA_CHUNK_TILES > 0 || chunk_tiles<DT, D>() == (D * (DT == PA_F32 ? 4 : 2) <= 256 ? 4 : 2),
+                  "chunk_min_tokens");
+    DecodeArgs args_copy = a;
+    void* args[] = {&args_copy};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_kernel<DT, D, B>), dim3(items), dim3(kChunkThreads),
+                           args, sizeof(int32_t) * (size_t)(a.num_seqs + 1), stream);
+}
+
+hipError_t dispatch_chunk(const DecodeArgs& a, const pa_cache_desc_t* cache, int items, hipStream_t stream) {
+    const int D = cache->head_dim, B = cache->block_size;
+#define PA_CHUNK_CASE(DT)                                                                              \
+    return D == 64 ? (B == 16 ? launch_chunk<DT, 64, 16>(a, items, stream) : launch_chunk<DT, 64, 32>(a, items, stream)) \
+                   : (B == 16 ? launch_chunk<DT, 128, 16>(a, items, stream)                           \
+                              : launch_chunk<DT, 128, 32>(a, items, stream));
+    switch (cache->dtype) {
+        case PA_F32:
+            PA_CHUNK_CASE(PA_F32)
+        case PA_F16:
+            PA_CHUNK_CASE(PA_F16)
+        default:
+            PA_CHUNK_CASE(PA_BF16)
+    }
+#undef PA_CHUNK_CASE
+}
+
 // Shared by pa_decode_ex, pa_decode_append (mode kModeAppend: k_new/v_new) and
 // pa_attend (mode kModeMulti: query_start and max_query_len).
 pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
@@ -1737,7 +2054,9 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     Plan plan;
     st = make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, tpc * G, &plan);
     if (st != PA_OK) return st;
-    if (plan.bytes > 0 && (workspace == nullptr || workspace_bytes < plan.bytes || !aligned(workspace, 256)))
+    // (several query tokens: chunk_kernel's item counter needs the synchronisation words in any case)
+    const size_t need = multi ? std::max(plan.bytes, (size_t)PA_WORKSPACE_SYNC_BYTES) : plan.bytes;
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256)))
         return PA_ERR_WORKSPACE;
 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -1797,10 +2116,25 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
                                     : dispatch_dtype<kModeDecode>(a, plan, cache, sm);
         return e == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
-    // Several query tokens: launch c takes tokens [c * tpc, (c + 1) * tpc) of every
-    // sequence, so each launch's pairs fit one 16-column tile; the launches share
-    // the workspace in stream order.
-    const int chunks = (max_query_len + tpc - 1) / tpc;
+    // Several query tokens.  Sequences with more than chunk_min tokens (a wave's
+    // column tiles' worth) go to chunk_kernel, one launch.  The others take the
+    // split path: launch c takes tokens [c * tpc, (c + 1) * tpc) of each, so each
+    // launch's pairs fit one 16-column tile; those launches share the workspace
+    // in stream order.
+    a.chunk_min = chunk_min_tokens(cache, tpc);
+    if (max_query_len > a.chunk_min) {
+        // Items: at most (rows / QB + num_seqs) x kv-heads; a workgroup per compute unit.
+        const int qb = a.chunk_min;  // an item's query tokens: its column tiles x tpc
+        const int64_t bound = ((int64_t)num_q_rows / qb + num_seqs) * cache->num_kv_heads;
+        if (bound >= (int64_t)INT32_MAX) return PA_ERR_UNSUPPORTED;
+        int cus = 0;
+        st = cu_count(&cus);
+        if (st != PA_OK) return st;
+        a.sync = reinterpret_cast<unsigned long long*>(ws);
+        const int grid = (int)std::min<int64_t>(bound, cus);
+        if (dispatch_chunk(a, cache, grid, sm) != hipSuccess) return PA_ERR_HIP;
+    }
+    const int chunks = (std::min(max_query_len, a.chunk_min) + tpc - 1) / tpc;
     for (int c = 0; c < chunks; ++c) {
         a.chunk = c;
         if (dispatch_dtype<kModeMulti>(a, plan, cache, sm) != hipSuccess) return PA_ERR_HIP;
@@ -1925,7 +2259,7 @@ size_t pa_attend_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
     Plan plan;
     const int cols = tokens_per_pair(num_q_heads, cache) * (num_q_heads / cache->num_kv_heads);
     if (make_plan(num_seqs, num_q_heads, max_blocks_per_seq, cache, num_workers, cols, &plan) != PA_OK) return 0;
-    return plan.bytes;
+    return std::max(plan.bytes, (size_t)PA_WORKSPACE_SYNC_BYTES);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,

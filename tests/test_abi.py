@@ -146,7 +146,7 @@ def test_attend_workspace_sizes():
     for Hq, cols in [(32, 16), (56, 14), (8, 16), (128, 16)]:  # G = 4, 7, 1, 16: floor(16/G) tokens x G heads
         got = L.pa_attend_workspace_bytes(S, Hq, 256, ctypes.byref(d), W_)
         assert got == SYNC + r(4 * waves * 2 * cols) + 4 * waves * 2 * cols * D
-    assert L.pa_attend_workspace_bytes(S, 32, 256, ctypes.byref(d), -1) == 0
+    assert L.pa_attend_workspace_bytes(S, 32, 256, ctypes.byref(d), -1) == SYNC  # the prompt-chunk item counter
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -10,7 +10,7 @@ import torch
 import oracle
 import paged_kv_decode_slot_amd as pa
 from paged_kv_decode_slot_amd import workloads as W
-from tests.gpu_helpers import TOL, GpuCase, dev_bits, log, max_abs_err
+from tests.gpu_helpers import TOL, GpuCase, check_output, dev_bits, log, max_abs_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -28,11 +28,16 @@ def _attend(g: GpuCase, mc: W.MultiCase, workers=0):
                      num_workers=workers)
 
 
-def _oracle(mc: W.MultiCase) -> np.ndarray:
+def _oracle(mc: W.MultiCase, with_abs_v: bool = False):
+    """The oracle's answer, and with with_abs_v also its softmax average of |V|
+    (the same attention with |V| in place of V), which the derived bound uses."""
     c = mc.base
     kp, vp = oracle.build_pools(c)
-    return oracle.attend(mc.q, kp, vp, c.block_tables, c.context_lens, mc.query_start, c.scale,
-                         Hkv=c.Hkv, B=c.B)
+    ref = oracle.attend(mc.q, kp, vp, c.block_tables, c.context_lens, mc.query_start, c.scale, Hkv=c.Hkv, B=c.B)
+    if not with_abs_v:
+        return ref
+    return ref, oracle.attend(mc.q, kp, vp.abs(), c.block_tables, c.context_lens, mc.query_start, c.scale,
+                              Hkv=c.Hkv, B=c.B)
 
 
 def _q_lens(case: W.Case, kind: str, seed: int) -> np.ndarray:
@@ -140,3 +145,47 @@ def test_attend_query_start_is_clamped_to_the_rows():
     torch.cuda.synchronize()
     assert torch.equal(dev_bits(out_full[:R]), dev_bits(good))
     assert bool((out_full[R:] == 7.0).all())
+
+
+# ---- prompt chunks: sequences with more query tokens than one chunk_kernel wave holds ----
+
+CHUNK_SHAPES = [
+    # Llama-3-8B-shaped layer: prompt chunks of 64 to 512 tokens beside decode tokens and drafts
+    (dict(S=12, Hq=32, Hkv=8, D=128, B=16, dtype="bf16", ctx_range=(600, 2500)),
+     [1, 1, 64, 128, 1, 256, 512, 1, 3, 17, 300, 1]),
+    # Qwen2-like G = 7 (2 tokens, 14 columns a tile), block 32, fp16
+    (dict(S=6, Hq=28, Hkv=4, D=128, B=32, dtype="f16", ctx_range=(300, 1400)), [1, 200, 33, 1, 96, 5]),
+    # TinyLlama-like G = 8, d64, f32 (two column tiles a wave)
+    (dict(S=5, Hq=32, Hkv=4, D=64, B=16, dtype="f32", ctx_range=(100, 700)), [70, 1, 2, 150, 9]),
+    # G = 1 (16 tokens a tile): whole prompts, lengths at block edges
+    (dict(S=6, Hq=4, Hkv=4, D=64, B=32, dtype="bf16", ctx=[65, 64, 129, 200, 31, 300]), [65, 64, 129, 200, 31, 300]),
+    # G = 16 (one token a tile), prompt longer than a block
+    (dict(S=3, Hq=16, Hkv=1, D=128, B=16, dtype="bf16", ctx=[90, 400, 17]), [90, 40, 17]),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(CHUNK_SHAPES)))
+def test_attend_prompt_chunks(idx):
+    kw, q_lens = CHUNK_SHAPES[idx]
+    case = W.make_case(seed=700 + idx, name=f"chunk{idx}", **kw)
+    mc = W.with_queries(case, q_lens, seed=800 + idx)
+    log(f"[chunks] shape {idx}: q_lens {mc.q_lens.tolist()}, ctx {case.context_lens.tolist()}")
+    g = _gpu(case)
+    out = _attend(g, mc)
+    again = _attend(g, mc)
+    torch.cuda.synchronize()
+    check_output(out, *_oracle(mc, True), case.dtype, f"[chunks] shape {idx}")
+    assert torch.equal(dev_bits(out), dev_bits(again))  # run to run, bitwise
+
+
+def test_attend_chunks_on_llama3_batch():
+    """The Llama-3-8B-shaped batch with 8 of its 64 sequences carrying prompt
+    chunks of 64 to 512 tokens and the rest one decode token each."""
+    case = W.config_case(3)
+    q_lens = np.ones(case.S, dtype=np.int64)
+    q_lens[::8] = [64, 96, 128, 200, 256, 300, 400, 512]
+    mc = W.with_queries(case, q_lens, seed=901)
+    log(f"[chunks] C3 with prompt chunks {mc.q_lens[::8].tolist()}")
+    out = _attend(_gpu(case), mc)
+    torch.cuda.synchronize()
+    check_output(out, *_oracle(mc, True), case.dtype, "[chunks] C3 mixed")
