@@ -268,14 +268,14 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
  *   num_q_rows     : host value, the rows of q and out
  *   other arguments as in pa_decode_ex; the workspace must hold
  *   pa_attend_workspace_bytes(...) bytes
- * Two paths, chosen per sequence on the device.  A sequence with at most
- * C = 4 x floor(16 / G) tokens (2 x for f32 with head_dim 128) takes the split
- * path of pa_decode_ex: its tokens floor(16 / G) at a time (one launch per
- * group, all on `stream`), each group a matrix-core tile that reads the K/V
- * its tokens see once.  A longer one (a prompt chunk) is cut into blocks of C
- * tokens, each attended by one workgroup whose four waves split the positions
- * and merge at the end: its K/V is read once per block (from HBM about once
- * in all, the blocks of a sequence running side by side).
+ * Two paths, chosen per sequence on the device, two launches on `stream`.
+ * A sequence with at most floor(16 / G) tokens takes the split path of
+ * pa_decode_ex: its tokens and heads are the columns of one matrix-core tile
+ * that reads the K/V they see once.  A longer one (draft tokens, a prompt
+ * chunk) is cut into blocks of C = 4 x floor(16 / G) tokens (2 x for f32 with
+ * head_dim 128), each attended by one workgroup whose four waves split the
+ * positions and merge at the end: its K/V is read once per block (from HBM
+ * about once in all, the blocks of a sequence running side by side).
  * Preconditions (unchecked): n <= L, and those of pa_decode.  A column whose
  * tokens see no position (only possible when n > L) gives 0.
  */

@@ -691,10 +691,12 @@ __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, i
                            int unit0, MergeLds& L) {
     constexpr int E = DT == PA_F32 ? 4 : 2;
     constexpr int PB = kMergeLoads / UPL;
-    const int lane = threadIdx.x & 63, NC = a.cols;
+    // A part holds a.cols columns (the stride of the layout); only the pair's
+    // first `active` ones hold a query, and only those are read and merged.
+    const int lane = threadIdx.x & 63, NS = a.cols, NC = active;
     const int NU = NC * D / 4;
     const int part_bytes = NC * D * 4;
-    const int lse_bytes = (int)(W * hs * 2 * NC * 4);  // every wave's two slots of NC log-sum-exps
+    const int lse_bytes = (int)(W * hs * 2 * NS * 4);  // every wave's two slots of NS log-sum-exps
     const __amdgpu_buffer_rsrc_t lse_r =
         __builtin_amdgcn_make_buffer_rsrc(a.part_lse, (short)0, lse_bytes, kBufferWord3);
 
@@ -715,7 +717,7 @@ __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, i
     // part's worker, and in it the wave of this pair's kv-head.
     auto part_loc = [&](int k) -> int64_t {
         const int64_t wk = unit_runs ? owner_of(F + k, U, W) : wa + k;
-        return (int64_t)part_index(wk * hs + wi, k == 0 ? first_slot : 0, NC, 0);
+        return (int64_t)part_index(wk * hs + wi, k == 0 ? first_slot : 0, NS, 0);
     };
     // Every slot of v is defined and read on every path (unused slots are zero
     // and weigh 0), so no load of the merge can be left pending where the
@@ -813,7 +815,7 @@ __device__ __attribute__((always_inline)) void merge_parts(const DecodeArgs& a, 
     // The owner of the first block used slot 0 if this pair was its first run,
     // i.e. its units begin at or after the pair's first unit Fv.
     const int first_slot = run_start(wa, U, W) >= Fv ? 0 : 1;
-    const int units = a.cols * D / 4;  // 16-byte output units of the pair
+    const int units = active * D / 4;  // 16-byte output units of the pair's active columns
     if (units <= kWave)
         merge_body<DT, D, 1, MQ>(a, s, kvh, row0, active, F, parts, wa, first_slot, unit_runs, U, W, hs, wi, 0, L);
     else if (units <= 2 * kWave)
@@ -1155,13 +1157,14 @@ __device__ __attribute__((always_inline)) void attend_run(const DecodeArgs& a, c
     }
     {
         // The partial's outputs as 16-byte stores with the agent-coherence bit
-        // (through a resource bounded to this part, so lanes past a.cols store nothing).
+        // (through a resource bounded to the part's active columns, so lanes of
+        // padding columns store nothing).
         const size_t part0 = part_index(wid, slot, a.cols, 0);
         const __amdgpu_buffer_rsrc_t po = __builtin_amdgcn_make_buffer_rsrc(a.part_o + part0 * D, (short)0,
-                                                                             a.cols * D * 4, kBufferWord3);
+                                                                             active * D * 4, kBufferWord3);
 #pragma unroll
         for (int c = 0; c < C::kVChunk; ++c) coherent_store4(po, (n * D + 16 * c + 4 * r) * 4, O[c] * inv);
-        if (n < a.cols && r == 0) coherent_store(a.part_lse + part0 + n, m + __log2f(lsum));
+        if (n < active && r == 0) coherent_store(a.part_lse + part0 + n, m + __log2f(lsum));
     }
     // Publish the partial (wait until its device-coherent stores are done),
     // then count it; the wave that stores the last part merges.
@@ -1989,9 +1992,8 @@ int tokens_per_pair(int num_q_heads, const pa_cache_desc_t* cache) {
     return G >= 16 ? 1 : 16 / G;
 }
 
-// Tokens of one chunk_kernel wave (its column tiles x tpc): sequences with more
-// query tokens than this take chunk_kernel.
-int chunk_min_tokens(const pa_cache_desc_t* cache, int tpc) {
+// Query tokens of one chunk_kernel item (its column tiles x tpc).
+int chunk_block_tokens(const pa_cache_desc_t* cache, int tpc) {
     const int row_bytes = cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2);
     return (PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (row_bytes <= 256 ? 4 : 2)) * tpc;
 }
@@ -1999,7 +2001,7 @@ int chunk_min_tokens(const pa_cache_desc_t* cache, int tpc) {
 template <int DT, int D, int B>
 hipError_t launch_chunk(const DecodeArgs& a, int items, hipStream_t stream) {
     static_assert(PA_CHUNK_TILES > 0 || chunk_tiles<DT, D>() == (D * (DT == PA_F32 ? 4 : 2) <= 256 ? 4 : 2),
-                  "chunk_min_tokens");
+                  "chunk_block_tokens");
     DecodeArgs args_copy = a;
     void* args[] = {&args_copy};
     return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_kernel<DT, D, B>), dim3(items), dim3(kChunkThreads),
@@ -2116,15 +2118,14 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
                                     : dispatch_dtype<kModeDecode>(a, plan, cache, sm);
         return e == hipSuccess ? PA_OK : PA_ERR_HIP;
     }
-    // Several query tokens.  Sequences with more than chunk_min tokens (a wave's
-    // column tiles' worth) go to chunk_kernel, one launch.  The others take the
-    // split path: launch c takes tokens [c * tpc, (c + 1) * tpc) of each, so each
-    // launch's pairs fit one 16-column tile; those launches share the workspace
-    // in stream order.
-    a.chunk_min = chunk_min_tokens(cache, tpc);
+    // Several query tokens.  Sequences with more tokens than one 16-column tile
+    // holds (tpc) go to chunk_kernel, one launch: on the split path they would
+    // take one launch, and one pass over their K/V, per group of tpc tokens.
+    // The others take the split path, one launch, a pair per 16-column tile.
+    a.chunk_min = tpc;
     if (max_query_len > a.chunk_min) {
         // Items: at most (rows / QB + num_seqs) x kv-heads; a workgroup per compute unit.
-        const int qb = a.chunk_min;  // an item's query tokens: its column tiles x tpc
+        const int qb = chunk_block_tokens(cache, tpc);  // an item's query tokens
         const int64_t bound = ((int64_t)num_q_rows / qb + num_seqs) * cache->num_kv_heads;
         if (bound >= (int64_t)INT32_MAX) return PA_ERR_UNSUPPORTED;
         int cus = 0;
