@@ -1432,8 +1432,8 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
 // merged through LDS at the end (the same log-sum-exp identity as the split
 // merge).  The grid is persistent, one workgroup per compute unit: each builds
 // the per-sequence prefix of item counts in LDS once and then takes items
-// from a counter in the workspace's synchronisation words (the last workgroup
-// to finish puts the counter back to zero).  Sequences with at most chunk_min
+// from counters in the workspace's synchronisation words, one per XCD (the
+// last workgroup to finish puts them back to zero).  Sequences with at most chunk_min
 // tokens are left to decode_kernel's several-token mode.
 constexpr int kChunkThreads = 256;
 constexpr int kChunkWaves = kChunkThreads / kWave;
@@ -1677,24 +1677,35 @@ __global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(DecodeArgs a) {
     __syncthreads();
     const int nitems = s_pre[S];
 
-    // Items in order (sequence, kv-head, query block), taken from the counter.
-    unsigned long long* counter = a.sync;
-    for (;;) {
-        if (tid == 0) s_item = (int)atomicAdd(counter, 1ull);
-        __syncthreads();
-        const int item = __builtin_amdgcn_readfirstlane(s_item);
-        __syncthreads();
-        if (item >= nitems) break;
-        const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, item));
-        const int nqb = (s_pre[s + 1] - s_pre[s]) / Hkv;
-        const int local = item - s_pre[s];
-        chunk_item<DT, D, B>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
+    // Items in order (sequence, kv-head, query block).  The items are cut into
+    // kXcds contiguous ranges, one per XCD (workgroups are dealt to the XCDs in
+    // turn, blockIdx % kXcds), each with a counter in the synchronisation words:
+    // a workgroup takes items from its own XCD's range, so the blocks of one
+    // (sequence, kv-head) run side by side and share K/V in that XCD's L2; when
+    // its range is used up it takes what is left of the others'.
+    constexpr int kXcds = 8;
+    unsigned long long* counter = a.sync;  // [kXcds] item counters, then the count of workgroups done
+    const int home = (int)(blockIdx.x % kXcds);
+    for (int v = 0; v < kXcds; ++v) {
+        const int x = (home + v) % kXcds;
+        const int lo_item = (int)((int64_t)nitems * x / kXcds), hi_item = (int)((int64_t)nitems * (x + 1) / kXcds);
+        for (;;) {
+            if (tid == 0) s_item = lo_item + (int)atomicAdd(counter + x, 1ull);
+            __syncthreads();
+            const int item = __builtin_amdgcn_readfirstlane(s_item);
+            __syncthreads();
+            if (item >= hi_item) break;
+            const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, item));
+            const int nqb = (s_pre[s + 1] - s_pre[s]) / Hkv;
+            const int local = item - s_pre[s];
+            chunk_item<DT, D, B>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
+        }
     }
-    // The last workgroup out puts the counter (and its own count) back to zero.
+    // The last workgroup out puts the counters (and the count) back to zero.
     if (tid == 0) {
-        if (atomicAdd(counter + 1, 1ull) + 1 == gridDim.x) {
-            atomicExch(counter, 0ull);
-            atomicExch(counter + 1, 0ull);
+        if (atomicAdd(counter + kXcds, 1ull) + 1 == gridDim.x) {
+#pragma unroll
+            for (int x = 0; x <= kXcds; ++x) atomicExch(counter + x, 0ull);
         }
     }
 }
