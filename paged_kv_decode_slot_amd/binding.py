@@ -17,6 +17,9 @@ _LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(os.path.dirname(os.p
                                                            "libpagedattn.so")
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP, PA_ERR_CAPACITY = range(6)
+# PA_ABI_VERSION of the C interface the signatures below are written for; a
+# library built from other sources is refused when it is loaded.
+ABI_VERSION = 3
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _ELT = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
 
@@ -145,6 +148,9 @@ def lib() -> ctypes.CDLL:
         L.pa_acct_retire.restype = ctypes.c_int
         L.pa_pool_telemetry.argtypes = [AP, P, ctypes.c_int64, ctypes.POINTER(PoolTelemetry)]
         L.pa_pool_telemetry.restype = ctypes.c_int
+        got = L.pa_abi_version()
+        if got != ABI_VERSION:
+            raise RuntimeError(f"{_LIB_PATH} has ABI {got}; this binding marshals ABI {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 

@@ -615,11 +615,10 @@ __device__ inline float row_group_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Per-wave LDS used by a merge: part weights of up to 64 parts, and the
-// per-head running maximum, denominator and rescale factor.
+// Per-wave LDS used by a merge: the weights of a pass's parts, and per column
+// the running denominator and rescale factor.
 struct MergeLds {
-    float w[kWave][kMaxGroup];  // weight of part k for head h (relative to the running max)
-    float M[kMaxGroup];         // running maximum of the parts' log-sum-exps (log2 domain)
+    float w[kWave][kMaxGroup];  // weight of part k for column h (relative to the running max)
     float den[kMaxGroup];       // running sum of weights
     float rescale[kMaxGroup];   // factor applied to earlier chunks when the running max grows
 };
@@ -633,6 +632,24 @@ template <int CTRL>
 __device__ inline float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
+// Max and sum over the lanes that share lane % NCp (NCp a power of two up to
+// 16): rotations inside each 16-lane row (xor 1, xor 2 by quad_perm; row_ror
+// 4 and 8), as many as NCp leaves, then across the four rows by the swaps.
+__device__ inline float parts_max(float x, int NCp) {
+    if (NCp < 2) x = fmaxf(x, dpp<0xB1>(x));
+    if (NCp < 4) x = fmaxf(x, dpp<0x4E>(x));
+    if (NCp < 8) x = fmaxf(x, dpp<0x124>(x));
+    if (NCp < 16) x = fmaxf(x, dpp<0x128>(x));
+    return row_group_max(x);
+}
+__device__ inline float parts_sum(float x, int NCp) {
+    if (NCp < 2) x += dpp<0xB1>(x);
+    if (NCp < 4) x += dpp<0x4E>(x);
+    if (NCp < 8) x += dpp<0x124>(x);
+    if (NCp < 16) x += dpp<0x128>(x);
+    return row_group_sum(x);
+}
+
 // Whole-wave reductions without LDS: all-reduce within each 16-lane row by DPP,
 // then across the four rows with the permlane swaps.
 __device__ inline float wave_max(float x) {
@@ -670,9 +687,10 @@ __device__ inline float coherent_load1(__amdgpu_buffer_rsrc_t r, int byte_offset
 // one.  A pair has NC = a.cols columns (heads, or query token x head); its
 // NC x D outputs are cut into 16-byte units; in a pass over units
 // [unit0, unit0 + 64 UPL), lane l owns units unit0 + l + 64 i (i < UPL) and
-// keeps their float4 accumulators in registers.  Parts are taken 64 at a
-// time: the lanes read one part's NC log-sum-exps each, and per column the
-// wave forms the running maximum M, the weights 2^(lse - M) and their sum.
+// keeps their float4 accumulators in registers.  Parts are taken 64 / NCp at a
+// time (NCp: NC rounded up to a power of two), one log-sum-exp per lane, and
+// one reduction over the lanes of each column forms the running maximum M, the
+// weights 2^(lse - M) and their sum for all columns at once.
 // The outputs are read PB = kMergeLoads/UPL parts per batch, kMergeLoads
 // 16-byte loads in flight per lane; the first batch is issued before the
 // log-sum-exps, so a merge of up to PB parts costs one round trip to memory.  Only the first
@@ -707,12 +725,6 @@ __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, i
         acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         hu[i] = min((unit0 + lane + kWave * i) * 4 / D, NC - 1);
     }
-    if (lane < kMaxGroup) {
-        L.M[lane] = -INFINITY;
-        L.den[lane] = 0.f;
-    }
-    __builtin_amdgcn_wave_barrier();
-
     // Index of part k's first log-sum-exp (part_index(wave, slot, NC, 0)): the
     // part's worker, and in it the wave of this pair's kv-head.
     auto part_loc = [&](int k) -> int64_t {
@@ -745,39 +757,36 @@ __device__ __attribute__((always_inline)) void merge_body(const DecodeArgs& a, i
         }
     };
 
-    for (int k0 = 0; k0 < parts; k0 += kWave) {
-        const int cnt = min(kWave, parts - k0);
+    // A pass takes PPP parts: lane (kk, hh) = (lane / NCp, lane % NCp) holds
+    // part k0 + kk's log-sum-exp of column hh (NCp: the columns rounded up to a
+    // power of two), so the maxima and sums over the parts of every column come
+    // from one reduction across the lanes of that column.  Mh and Dh are the
+    // column's running maximum and denominator (the same in all its lanes).
+    const int NCp = NC <= 1 ? 1 : NC <= 2 ? 2 : NC <= 4 ? 4 : NC <= 8 ? 8 : 16;
+    const int PPP = kWave / NCp;
+    const int kk = lane / NCp, hh = lane % NCp;
+    float Mh = -INFINITY, Dh = 0.f;
+    for (int k0 = 0; k0 < parts; k0 += PPP) {
+        const int cnt = min(PPP, parts - k0);
         issue(k0, min(PB, cnt));
-        // Lane k reads part k0 + k's log-sum-exps.  The loads are not under a
-        // lane mask (a lane without a part reads past the end and gets 0), so
-        // the compiler sees every one of them consumed.
-        const bool has = lane < cnt;
-        const int lse_off = has ? (int)(part_loc(k0 + lane) * 4) : lse_bytes;
-        float l[kMaxGroup];
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-            const float x = coherent_load1(lse_r, lse_off + 4 * h);
-            l[h] = (has && h < NC) ? x : -INFINITY;
+        // The load is not under a lane mask (a lane without a part reads past
+        // the end and gets 0), so the compiler sees every one consumed.
+        const bool has = kk < cnt && hh < NC;
+        const int lse_off = has ? (int)(part_loc(k0 + kk) * 4) + 4 * hh : lse_bytes;
+        const float x0 = coherent_load1(lse_r, lse_off);
+        const float x = has ? x0 : -INFINITY;
+        const float mn = fmaxf(Mh, parts_max(x, NCp));
+        // (0 while Mh is -inf; a padding column, all -inf, keeps 1)
+        const float sc = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(Mh - mn);
+        const float wt = has ? __builtin_amdgcn_exp2f(x - mn) : 0.f;
+        Dh = Dh * sc + parts_sum(wt, NCp);
+        Mh = mn;
+        L.w[kk][hh] = wt;
+        if (kk == 0) {
+            L.den[hh] = Dh;
+            L.rescale[hh] = sc;
         }
-        for (int h = 0; h < NC; ++h) {
-            float lh = l[0];
-#pragma unroll
-            for (int i = 1; i < kMaxGroup; ++i)
-                if (i == h) lh = l[i];
-            const float m_old = L.M[h];
-            const float mn = fmaxf(m_old, wave_max(lh));
-            const float sc = __builtin_amdgcn_exp2f(m_old - mn);  // 0 while m_old is -inf
-            const float wt = has ? __builtin_amdgcn_exp2f(lh - mn) : 0.f;
-            const float dn = L.den[h] * sc + wave_sum(wt);
-            L.w[lane][h] = wt;
-            __builtin_amdgcn_wave_barrier();
-            if (lane == 0) {
-                L.M[h] = mn;
-                L.den[h] = dn;
-                L.rescale[h] = sc;
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
+        __builtin_amdgcn_wave_barrier();
         if (k0 > 0) {
 #pragma unroll
             for (int i = 0; i < UPL; ++i) acc[i] *= L.rescale[hu[i]];
