@@ -272,10 +272,10 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
  * A sequence with at most floor(16 / G) tokens takes the split path of
  * pa_decode_ex: its tokens and heads are the columns of one matrix-core tile
  * that reads the K/V they see once.  A longer one (draft tokens, a prompt
- * chunk) is cut into blocks of C = 4 x floor(16 / G) tokens (2 x for f32 with
- * head_dim 128), each attended by one workgroup whose four waves split the
- * positions and merge at the end: its K/V is read once per block (from HBM
- * about once in all, the blocks of a sequence running side by side).
+ * chunk) is cut into blocks of C = 4 x floor(16 / G) tokens for 64-dim 16-bit
+ * rows and 2 x floor(16 / G) otherwise, each attended by one workgroup whose
+ * four waves split the positions and merge at the end: its K/V is read once
+ * per block (mostly from L2, the blocks of a sequence running side by side).
  * Preconditions (unchecked): n <= L, and those of pa_decode.  A column whose
  * tokens see no position (only possible when n > L) gives 0.
  */

@@ -412,13 +412,16 @@ typedef const int32_t __attribute__((address_space(4)))* ScalarPtr;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-template <typename T>
+// K/V loads.  The decode reads each K/V byte once, so its loads carry the
+// non-temporal hint; the prompt-chunk kernel reads a sequence's K/V once per
+// block of query tokens, and those blocks run side by side, so its loads are
+// plain and the repeats come from L2 (REUSE).
+template <typename T, bool REUSE = false>
 __device__ inline T load_kv(const uint8_t* p) {
-#if PA_KV_NONTEMPORAL
-    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
-#else
-    return *reinterpret_cast<const T*>(p);
-#endif
+    if constexpr (PA_KV_NONTEMPORAL && !REUSE)
+        return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+    else
+        return *reinterpret_cast<const T*>(p);
 }
 
 // Put one token's entries (token e of the piece's 4-token groups) into a V piece:
@@ -875,7 +878,7 @@ __device__ inline void load_q(const DecodeArgs& a, const Run& r, uint4* qf) {
 // The loads of tile `tau` of a run whose current block id is `phys`: the
 // 16-token slab tau % kSub of (block, kv-head), 16 * D contiguous elements of
 // either pool.
-template <int DT, int D, int B>
+template <int DT, int D, int B, bool REUSE = false>
 __device__ inline void load_tile(const DecodeArgs& a, int phys, int kvh, int u, Tile<DT, D, B>& t) {
     using C = Cfg<DT, D, B>;
     const int lane = threadIdx.x & 63, n = lane & 15, r = lane >> 4;
@@ -885,10 +888,10 @@ __device__ inline void load_tile(const DecodeArgs& a, int phys, int kvh, int u, 
     const uint8_t* vt = a.v_cache + slab;
 #pragma unroll
     for (int f = 0; f < C::kKFrag; ++f)
-        t.k[f] = __builtin_bit_cast(uint4, load_kv<u32x4>(kt + ((4 * f + r) * 16 + n) * 16));
+        t.k[f] = __builtin_bit_cast(uint4, load_kv<u32x4, REUSE>(kt + ((4 * f + r) * 16 + n) * 16));
 #pragma unroll
     for (int c = 0; c < C::kVPiece; ++c)
-        t.v[c] = __builtin_bit_cast(uint4, load_kv<u32x4>(vt + ((r * C::kVPiece + c) * 16 + n) * 16));
+        t.v[c] = __builtin_bit_cast(uint4, load_kv<u32x4, REUSE>(vt + ((r * C::kVPiece + c) * 16 + n) * 16));
 }
 
 // Start run r early: its first block id (already read: id0) and the one after,
@@ -1439,7 +1442,8 @@ __global__ __launch_bounds__(kGroupThreads, PA_MIN_WAVES_PER_SIMD) void decode_k
 // into four contiguous ranges of 16-token tiles, each read once, with the
 // online softmax of the split path per column; the four partial states are
 // merged through LDS at the end (the same log-sum-exp identity as the split
-// merge).  The grid is persistent, one workgroup per compute unit: each builds
+// merge).  The grid is persistent, as many workgroups per compute unit as
+// stay resident (chunk_occupancy): each builds
 // the per-sequence prefix of item counts in LDS once and then takes items
 // from counters in the workspace's synchronisation words, one per XCD (the
 // last workgroup to finish puts them back to zero).  Sequences with at most chunk_min
@@ -1450,10 +1454,25 @@ constexpr int kChunkWaves = kChunkThreads / kWave;
 #ifndef PA_CHUNK_TILES
 #define PA_CHUNK_TILES 0  // 0: by row size
 #endif
-// Column tiles per workgroup: as many as registers hold beside the K/V tile ring.
+#ifndef PA_CHUNK_REUSE
+#define PA_CHUNK_REUSE 1  // K/V loads without the non-temporal hint (query blocks share them in L2)
+#endif
+#ifndef PA_CHUNK_OCC
+#define PA_CHUNK_OCC 0  // resident workgroups per compute unit; 0: by row size
+#endif
+// Column tiles per workgroup and resident workgroups per compute unit: as many
+// tiles as fit, beside the K/V tile ring, in the registers of two waves per
+// SIMD (one wave per SIMD cannot overlap one wave's matrix products, softmax
+// and load waits: on the Llama-3-8B-shaped prompt chunks, 4 tiles at one wave
+// per SIMD took 235 us, 2 tiles at two 179 us).  f32 rows of 128 dims leave
+// room for two tiles at one wave per SIMD only.
 template <int DT, int D>
 constexpr int chunk_tiles() {
-    return PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (D * (DT == PA_F32 ? 4 : 2) <= 256 ? 4 : 2);
+    return PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (D * (DT == PA_F32 ? 4 : 2) <= 128 ? 4 : 2);
+}
+template <int DT, int D>
+constexpr int chunk_occupancy() {
+    return PA_CHUNK_OCC > 0 ? PA_CHUNK_OCC : (D * (DT == PA_F32 ? 4 : 2) <= 256 ? 2 : 1);
 }
 
 // Query rows of sequence i (query_start clamped into [0, num_q_rows]).
@@ -1526,7 +1545,7 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
             phys = ((unsigned)next_id < (unsigned)a.num_blocks) ? next_id : 0;
             if (j + 1 < nblk) next_id = bt[j + 1];
         }
-        load_tile<DT, D, B>(a, phys, g, u, t);
+        load_tile<DT, D, B, (bool)PA_CHUNK_REUSE>(a, phys, g, u, t);
     };
     // One tile: all NT score tiles first (independent products the matrix core
     // can overlap), then the softmax of every column with one rarely taken
@@ -1645,7 +1664,7 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
 }
 
 template <int DT, int D, int B>
-__global__ __launch_bounds__(kChunkThreads, 1) void chunk_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chunk_kernel(DecodeArgs a) {
     using C = Cfg<DT, D, B>;
     constexpr int NT = chunk_tiles<DT, D>();
     // The merge area: waves 1..3 hand one column tile's state to wave 0 at a time.
@@ -2015,25 +2034,29 @@ int tokens_per_pair(int num_q_heads, const pa_cache_desc_t* cache) {
 // Query tokens of one chunk_kernel item (its column tiles x tpc).
 int chunk_block_tokens(const pa_cache_desc_t* cache, int tpc) {
     const int row_bytes = cache->head_dim * (cache->dtype == PA_F32 ? 4 : 2);
-    return (PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (row_bytes <= 256 ? 4 : 2)) * tpc;
+    return (PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (row_bytes <= 128 ? 4 : 2)) * tpc;
 }
 
+// The persistent grid: resident workgroups per CU times the CUs, or fewer when
+// there are fewer items than that.
 template <int DT, int D, int B>
-hipError_t launch_chunk(const DecodeArgs& a, int items, hipStream_t stream) {
-    static_assert(PA_CHUNK_TILES > 0 || chunk_tiles<DT, D>() == (D * (DT == PA_F32 ? 4 : 2) <= 256 ? 4 : 2),
+hipError_t launch_chunk(const DecodeArgs& a, int64_t items, int cus, hipStream_t stream) {
+    const int grid = (int)std::min<int64_t>(items, (int64_t)cus * chunk_occupancy<DT, D>());
+    static_assert(PA_CHUNK_TILES > 0 || chunk_tiles<DT, D>() == (D * (DT == PA_F32 ? 4 : 2) <= 128 ? 4 : 2),
                   "chunk_block_tokens");
     DecodeArgs args_copy = a;
     void* args[] = {&args_copy};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_kernel<DT, D, B>), dim3(items), dim3(kChunkThreads),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_kernel<DT, D, B>), dim3(grid), dim3(kChunkThreads),
                            args, sizeof(int32_t) * (size_t)(a.num_seqs + 1), stream);
 }
 
-hipError_t dispatch_chunk(const DecodeArgs& a, const pa_cache_desc_t* cache, int items, hipStream_t stream) {
+hipError_t dispatch_chunk(const DecodeArgs& a, const pa_cache_desc_t* cache, int64_t items, int cus,
+                          hipStream_t stream) {
     const int D = cache->head_dim, B = cache->block_size;
 #define PA_CHUNK_CASE(DT)                                                                              \
-    return D == 64 ? (B == 16 ? launch_chunk<DT, 64, 16>(a, items, stream) : launch_chunk<DT, 64, 32>(a, items, stream)) \
-                   : (B == 16 ? launch_chunk<DT, 128, 16>(a, items, stream)                           \
-                              : launch_chunk<DT, 128, 32>(a, items, stream));
+    return D == 64 ? (B == 16 ? launch_chunk<DT, 64, 16>(a, items, cus, stream) : launch_chunk<DT, 64, 32>(a, items, cus, stream)) \
+                   : (B == 16 ? launch_chunk<DT, 128, 16>(a, items, cus, stream)                           \
+                              : launch_chunk<DT, 128, 32>(a, items, cus, stream));
     switch (cache->dtype) {
         case PA_F32:
             PA_CHUNK_CASE(PA_F32)
@@ -2152,8 +2175,7 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
         st = cu_count(&cus);
         if (st != PA_OK) return st;
         a.sync = reinterpret_cast<unsigned long long*>(ws);
-        const int grid = (int)std::min<int64_t>(bound, cus);
-        if (dispatch_chunk(a, cache, grid, sm) != hipSuccess) return PA_ERR_HIP;
+        if (dispatch_chunk(a, cache, bound, cus, sm) != hipSuccess) return PA_ERR_HIP;
     }
     const int chunks = (std::min(max_query_len, a.chunk_min) + tpc - 1) / tpc;
     for (int c = 0; c < chunks; ++c) {
