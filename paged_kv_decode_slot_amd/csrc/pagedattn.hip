@@ -68,10 +68,11 @@ constexpr int kWavesPerCU = PA_WAVES_PER_CU;  // automatic split: decode waves p
 #endif
 constexpr int kMinBlocksPerWorker = PA_MIN_BLOCKS_PER_WORKER;
 // Synchronisation words at the start of every workspace (zero before the first
-// call, and left zero by every call): kSyncHeader counters, then one arrival
-// word per (range, wave) of a split.
+// call, and left zero by every call): kSyncHeader counters (the prompt-chunk
+// kernel's item counters, one per XCD, and its count of workgroups done), then
+// one arrival word per (range, wave) of a split.
 constexpr int kSyncWords = PA_WORKSPACE_SYNC_BYTES / 8;
-constexpr int kSyncHeader = 8;
+constexpr int kSyncHeader = 16;
 constexpr int kMaxWorkers = 1 << 20;
 constexpr int kMaxRopePairs = 64;  // head_dim / 2
 #ifndef PA_RUN_COST_BYTES
@@ -1549,10 +1550,14 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
     };
     // One tile: all NT score tiles first (independent products the matrix core
     // can overlap), then the softmax of every column with one rarely taken
-    // branch for the rescales, then all NT PV products.
-    auto consume = [&](int tau, Tile<DT, D, B>& t) {
+    // branch for the rescales, then all NT PV products.  Only the tiles from
+    // tau_mask on hold positions some column must not see (past its token, or
+    // past the context); the others take the form without masks (`partial`
+    // false), where every score is finite and so is the running maximum after
+    // the first tile.
+    auto consume = [&](int tau, Tile<DT, D, B>& t, auto partial_tag) {
+        constexpr bool partial = decltype(partial_tag)::value;
         const int tok0 = 16 * tau + 4 * r;  // position of this lane's first row
-        const bool partial = tau >= tau_mask;
         f32x4 sc[NT];
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) {
@@ -1560,7 +1565,7 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
 #pragma unroll
             for (int f = 0; f < C::kKFrag; ++f) sc[ct] = qk_step<DT>(t.k[f], qf[ct][f], sc[ct]);
         }
-        if (partial) {
+        if constexpr (partial) {
 #pragma unroll
             for (int c = 0; c < C::kVPiece; ++c) mask_v<E>(t.v[c], tok0, L);
         }
@@ -1571,7 +1576,9 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 z[ct][e] = sc[ct][e] * a.scale_log2;
-                if (partial && tok0 + e > lim[ct]) z[ct][e] = -INFINITY;
+                if constexpr (partial) {
+                    if (tok0 + e > lim[ct]) z[ct][e] = -INFINITY;
+                }
             }
             tmax[ct] = row_group_max(fmaxf(fmaxf(z[ct][0], z[ct][1]), fmaxf(z[ct][2], z[ct][3])));
             up = up || tmax[ct] > m[ct] + kLazy;
@@ -1594,7 +1601,12 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
         for (int ct = 0; ct < NT; ++ct) {
             float p[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) p[e] = (z[ct][e] > -INFINITY) ? __builtin_amdgcn_exp2f(z[ct][e] - m[ct]) : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (partial)
+                    p[e] = (z[ct][e] > -INFINITY) ? __builtin_amdgcn_exp2f(z[ct][e] - m[ct]) : 0.f;
+                else
+                    p[e] = __builtin_amdgcn_exp2f(z[ct][e] - m[ct]);
+            }
             lsum[ct] += (p[0] + p[1]) + (p[2] + p[3]);
             pp[ct] = pack_p<DT>(p);
         }
@@ -1608,17 +1620,25 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
     // Two tiles in registers: the next one's loads are in flight while one is
     // consumed.  Every step issues a load (the last tile again at the very
     // end, unused), so no load sits under a branch.
+    // Pairs of tiles that lie before tau_mask take the form without masks; the
+    // rest (the masked form is exact for any tile) follow in the same ring.
     Tile<DT, D, B> buf[2];
     if (tau_lo < tau_hi) {
         issue(tau_lo, buf[0]);
         int tau = tau_lo;
+        for (; tau + 1 < tau_mask && tau + 1 < tau_hi; tau += 2) {
+            issue(tau + 1, buf[1]);
+            consume(tau, buf[0], std::false_type{});
+            issue(min(tau + 2, tau_hi - 1), buf[0]);
+            consume(tau + 1, buf[1], std::false_type{});
+        }
         for (; tau + 1 < tau_hi; tau += 2) {
             issue(tau + 1, buf[1]);
-            consume(tau, buf[0]);
+            consume(tau, buf[0], std::true_type{});
             issue(min(tau + 2, tau_hi - 1), buf[0]);
-            consume(tau + 1, buf[1]);
+            consume(tau + 1, buf[1], std::true_type{});
         }
-        if (tau < tau_hi) consume(tau, buf[0]);
+        if (tau < tau_hi) consume(tau, buf[0], std::true_type{});
     }
     wait_vmem_done();
 
@@ -1712,6 +1732,7 @@ __global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chu
     // (sequence, kv-head) run side by side and share K/V in that XCD's L2; when
     // its range is used up it takes what is left of the others'.
     constexpr int kXcds = 8;
+    static_assert(kXcds + 1 <= kSyncHeader, "the counters lie in the header of the synchronisation words");
     unsigned long long* counter = a.sync;  // [kXcds] item counters, then the count of workgroups done
     const int home = (int)(blockIdx.x % kXcds);
     for (int v = 0; v < kXcds; ++v) {
@@ -2175,6 +2196,10 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
         st = cu_count(&cus);
         if (st != PA_OK) return st;
         a.sync = reinterpret_cast<unsigned long long*>(ws);
+#if PA_ATTEND_ALL_CHUNK
+        a.chunk_min = 0;
+        return dispatch_chunk(a, cache, bound, cus, sm) == hipSuccess ? PA_OK : PA_ERR_HIP;
+#endif
         if (dispatch_chunk(a, cache, bound, cus, sm) != hipSuccess) return PA_ERR_HIP;
     }
     const int chunks = (std::min(max_query_len, a.chunk_min) + tpc - 1) / tpc;
