@@ -185,7 +185,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * A worker is one workgroup with a wavefront per kv-head of a slice of the
  * kv-heads (the slice is the largest divisor of num_kv_heads up to 2), so
  * every wave of a worker covers the same logical blocks.  num_workers times
- * the slice may be at most PA_WORKSPACE_SYNC_BYTES / 8 - 8 (the arrival words
+ * the slice may be at most PA_WORKSPACE_SYNC_BYTES / 8 - 16 (the arrival words
  * of the split), else PA_ERR_UNSUPPORTED.
  * Every choice computes the same function; results agree within rounding.
  */

@@ -2196,10 +2196,6 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
         st = cu_count(&cus);
         if (st != PA_OK) return st;
         a.sync = reinterpret_cast<unsigned long long*>(ws);
-#if PA_ATTEND_ALL_CHUNK
-        a.chunk_min = 0;
-        return dispatch_chunk(a, cache, bound, cus, sm) == hipSuccess ? PA_OK : PA_ERR_HIP;
-#endif
         if (dispatch_chunk(a, cache, bound, cus, sm) != hipSuccess) return PA_ERR_HIP;
     }
     const int chunks = (std::min(max_query_len, a.chunk_min) + tpc - 1) / tpc;

@@ -200,10 +200,10 @@ def test_sync_region_size_matches_the_header():
 
 
 def test_worker_count_bounded_by_the_arrival_words():
-    # one arrival word per wave of every worker, after 8 header words
+    # one arrival word per wave of every worker, after 16 header words
     L = pa.lib()
     d = _desc(head_dim=128, num_kv_heads=8)  # slices of 2 kv-heads: 2 waves per worker
-    most = (SYNC // 8 - 8) // 2
+    most = (SYNC // 8 - 16) // 2
     assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), most) > 0
     assert L.pa_decode_workspace_bytes_ex(64, 32, 256, ctypes.byref(d), most + 1) == 0
     assert _decode(_desc(num_kv_heads=2), workers=most + 1) == UNSUPPORTED  # rejected before any launch
