@@ -1482,8 +1482,10 @@ __device__ inline void query_rows(const DecodeArgs& a, int i, int& q0, int& nq) 
     nq = min(max(a.query_start[i + 1], q0), a.num_q_rows) - q0;
 }
 
-// The attention of one item: sequence s, kv-head g, query block qb.
-template <int DT, int D, int B>
+// The attention of one item: sequence s, kv-head g, query block qb.  REUSE:
+// other query blocks of the sequence read the same K/V (plain loads, kept in
+// L2); otherwise the loads carry the non-temporal hint, as in the decode.
+template <int DT, int D, int B, bool REUSE>
 __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, int s, int g, int qb, f32x4 (*s_o)[Cfg<DT, D, B>::kVChunk][kWave],
                                                           float (*s_m)[kWave], float (*s_l)[kWave]) {
     using C = Cfg<DT, D, B>;
@@ -1546,7 +1548,7 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
             phys = ((unsigned)next_id < (unsigned)a.num_blocks) ? next_id : 0;
             if (j + 1 < nblk) next_id = bt[j + 1];
         }
-        load_tile<DT, D, B, (bool)PA_CHUNK_REUSE>(a, phys, g, u, t);
+        load_tile<DT, D, B, REUSE && (bool)PA_CHUNK_REUSE>(a, phys, g, u, t);
     };
     // One tile: all NT score tiles first (independent products the matrix core
     // can overlap), then the softmax of every column with one rarely taken
@@ -1747,7 +1749,10 @@ __global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chu
             const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, item));
             const int nqb = (s_pre[s + 1] - s_pre[s]) / Hkv;
             const int local = item - s_pre[s];
-            chunk_item<DT, D, B>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
+            if (nqb > 1)
+                chunk_item<DT, D, B, true>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
+            else
+                chunk_item<DT, D, B, false>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
         }
     }
     // The last workgroup out puts the counters (and the count) back to zero.
