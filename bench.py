@@ -35,6 +35,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention: achieved HBM GB/s (% of peak) and μs per layer-step"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+# Dense matrix-core peaks of MI355X (AMD's published figures, without sparsity), TFLOP/s.
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 
 
 def log(msg):
@@ -247,12 +249,18 @@ def measure_chunks(n, args, device):
     flops = 4 * seen * case.Hq * case.D
     b = W.attend_bytes(mc)
     rows = int(mc.query_start[-1])
+    tflops = flops / (us * 1e-6) / 1e12
+    c = measured_counters(n, "chunks")
     return dict(workload=W.CONFIGS[n]["name"], query_lens=f"{int(chunk.sum())} prompt chunks {ql[chunk].tolist()}, "
                 f"{int((~chunk).sum())} decode tokens", us=round(us, 2), query_rows=rows,
-                query_rows_per_s=round(rows / (us * 1e-6)), chunk_tflops=round(flops / (us * 1e-6) / 1e12, 1),
+                query_rows_per_s=round(rows / (us * 1e-6)), chunk_tflops=round(tflops, 1),
+                chunk_frac_of_mfma_peak=round(tflops / MFMA_PEAK_TFLOPS[case.dtype], 4),
                 bytes=b, gbs=round(b / (us * 1e-6) / 1e9, 1),
+                chunk_kernel_traffic=None if c is None else c["total"],
                 note="one pa_attend call: chunk_kernel for the chunks, the split path for the decode tokens; "
-                     "chunk_tflops counts only the chunks' causal FLOPs over the whole call's time")
+                     "chunk_tflops counts only the chunks' causal FLOPs over the whole call's time, against the "
+                     "dense matrix-core peak of the dtype; chunk_kernel_traffic: counter bytes of the chunk "
+                     "kernel's launch alone")
 
 
 def measure_rope(n, theta, args, device):
@@ -388,7 +396,8 @@ TRAFFIC_FILES = {(3, "fused"): "profiles/decode_append_kernel_C3_llama3-8b_bf16_
                  (3, "attend4"): "profiles/attend_kernel_C3_llama3-8b_4tokens_bf16_counters.txt",
                  (3, "rope"): "profiles/decode_rope_append_kernel_C3_llama3-8b_bf16_counters.txt",
                  (4, "fused"): "profiles/decode_append_kernel_C4_ragged_bf16_counters.txt",
-                 (5, "fused"): "profiles/decode_append_kernel_C5_long_bf16_counters.txt"}
+                 (5, "fused"): "profiles/decode_append_kernel_C5_long_bf16_counters.txt",
+                 (3, "chunks"): "profiles/chunk_kernel_C3_prompt_chunks_bf16_counters.txt"}
 KERNEL_SOURCE = "paged_kv_decode_slot_amd/csrc/pagedattn.hip"
 
 
