@@ -161,6 +161,9 @@ CHUNK_SHAPES = [
     (dict(S=6, Hq=4, Hkv=4, D=64, B=32, dtype="bf16", ctx=[65, 64, 129, 200, 31, 300]), [65, 64, 129, 200, 31, 300]),
     # G = 16 (one token a tile), prompt longer than a block
     (dict(S=3, Hq=16, Hkv=1, D=128, B=16, dtype="bf16", ctx=[90, 400, 17]), [90, 40, 17]),
+    # G = 4: 5..8 tokens fill one query block (the chunk kernel's single-block form),
+    # 9 and 16 two, 1 goes to the split path
+    (dict(S=7, Hq=32, Hkv=8, D=128, B=16, dtype="bf16", ctx_range=(20, 900)), [5, 6, 7, 8, 1, 9, 16]),
 ]
 
 
@@ -189,3 +192,17 @@ def test_attend_chunks_on_llama3_batch():
     out = _attend(_gpu(case), mc)
     torch.cuda.synchronize()
     check_output(out, *_oracle(mc, True), case.dtype, "[chunks] C3 mixed")
+
+
+def test_attend_drafts_on_llama3_batch():
+    """Eight draft tokens on each of the 64 sequences of the Llama-3-8B-shaped batch:
+    every sequence is one query block of the prompt-chunk kernel."""
+    case = W.config_case(3)
+    mc = W.with_queries(case, np.full(case.S, 8), seed=911)
+    log("[chunks] C3 with 8 query tokens per sequence")
+    g = _gpu(case)
+    out = _attend(g, mc)
+    again = _attend(g, mc)
+    torch.cuda.synchronize()
+    check_output(out, *_oracle(mc, True), case.dtype, "[chunks] C3 8 each")
+    assert torch.equal(dev_bits(out), dev_bits(again))
