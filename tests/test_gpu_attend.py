@@ -206,3 +206,20 @@ def test_attend_drafts_on_llama3_batch():
     torch.cuda.synchronize()
     check_output(out, *_oracle(mc, True), case.dtype, "[chunks] C3 8 each")
     assert torch.equal(dev_bits(out), dev_bits(again))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attend_negative_scale(dtype):
+    """A negative scale (the softmax of -q.k) on both paths: draft tokens on the
+    split path and prompt chunks on the prompt-chunk kernel."""
+    case = W.make_case(S=5, Hq=8, Hkv=2, D=128, B=16, dtype=dtype, ctx_range=(40, 700), seed=931, name="neg")
+    mc = W.with_queries(case, [2, 40, 1, 17, 9], seed=932)
+    neg = -case.scale
+    g = _gpu(case)
+    qs = torch.from_numpy(mc.query_start).to(DEV)
+    log(f"[attend] negative scale {neg}, {dtype}, q_lens {mc.q_lens.tolist()}")
+    out = pa.attend(mc.q.to(DEV), g.k_cache, g.v_cache, g.bt, g.ctx, qs, mc.max_q_len, neg)
+    torch.cuda.synchronize()
+    kp, vp = oracle.build_pools(case)
+    ref = oracle.attend(mc.q, kp, vp, case.block_tables, case.context_lens, mc.query_start, neg, Hkv=case.Hkv, B=case.B)
+    assert max_abs_err(out, ref) <= TOL[case.dtype]
