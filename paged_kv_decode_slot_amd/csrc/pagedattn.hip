@@ -1486,7 +1486,8 @@ __device__ inline void query_rows(const DecodeArgs& a, int i, int& q0, int& nq) 
 // other query blocks of the sequence read the same K/V (plain loads, kept in
 // L2); otherwise the loads carry the non-temporal hint, as in the decode.
 template <int DT, int D, int B, bool REUSE>
-__device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, int s, int g, int qb, f32x4 (*s_o)[Cfg<DT, D, B>::kVChunk][kWave],
+__device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, int s, int g, int qb, int q0, int nq,
+                                                          int L, f32x4 (*s_o)[Cfg<DT, D, B>::kVChunk][kWave],
                                                           float (*s_m)[kWave], float (*s_l)[kWave]) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
@@ -1496,10 +1497,7 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
     const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int G = a.group, tpc = a.tpc;
     const int QB = NT * tpc;  // query tokens of a workgroup
-    int q0, nq;
-    query_rows(a, s, q0, nq);
     const int i_begin = qb * QB;  // the item's first token
-    const int L = clamp_ctx(a.context_lens[s], B, a.max_blocks);
     const int ntok = min(QB, nq - i_begin);
 
     // Per column tile: the lane's token (padding columns and tokens past the
@@ -1695,11 +1693,15 @@ __global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chu
     __shared__ int32_t s_wave_tot[kChunkWaves];
     __shared__ int32_t s_item;
     extern __shared__ __attribute__((aligned(16))) int32_t s_pre[];  // [num_seqs + 1]: items before sequence s
+    int32_t* s_q0 = s_pre + a.num_seqs + 1;  // [num_seqs + 1]: first query row (clamped)
+    int32_t* s_len = s_q0 + a.num_seqs + 1;  // [num_seqs]: context length (clamped)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = a.num_seqs, Hkv = a.num_kv_heads, QB = NT * a.tpc;
     // Items of a sequence: its query blocks times the kv-heads, when it has
-    // more than chunk_min tokens.  Exclusive prefix over sequences into LDS.
+    // more than chunk_min tokens.  Exclusive prefix over sequences into LDS,
+    // beside each sequence's first query row and length, so that an item
+    // starts from LDS rather than from memory.
     auto items_of = [&](int i) {
         int q0, nq;
         query_rows(a, i, q0, nq);
@@ -1708,7 +1710,14 @@ __global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chu
     const int per = (S + kChunkThreads - 1) / kChunkThreads;
     const int lo = min(S, tid * per), hi = min(S, lo + per);
     int sum = 0;
-    for (int i = lo; i < hi; ++i) sum += items_of(i);
+    for (int i = lo; i < hi; ++i) {
+        int q0, nq;
+        query_rows(a, i, q0, nq);
+        s_q0[i] = q0;
+        s_len[i] = clamp_ctx(a.context_lens[i], B, a.max_blocks);
+        sum += items_of(i);
+    }
+    if (tid == 0) s_q0[S] = min(max(a.query_start[S], 0), a.num_q_rows);
     int x = sum;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -1749,10 +1758,13 @@ __global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chu
             const int s = __builtin_amdgcn_readfirstlane(find_seq(s_pre, S, item));
             const int nqb = (s_pre[s + 1] - s_pre[s]) / Hkv;
             const int local = item - s_pre[s];
+            const int q0 = __builtin_amdgcn_readfirstlane(s_q0[s]);
+            const int nq = max(__builtin_amdgcn_readfirstlane(s_q0[s + 1]), q0) - q0;
+            const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
             if (nqb > 1)
-                chunk_item<DT, D, B, true>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
+                chunk_item<DT, D, B, true>(a, s, local / nqb, local % nqb, q0, nq, L, s_o, s_m, s_l);
             else
-                chunk_item<DT, D, B, false>(a, s, local / nqb, local % nqb, s_o, s_m, s_l);
+                chunk_item<DT, D, B, false>(a, s, local / nqb, local % nqb, q0, nq, L, s_o, s_m, s_l);
         }
     }
     // The last workgroup out puts the counters (and the count) back to zero.
@@ -2063,6 +2075,13 @@ int chunk_block_tokens(const pa_cache_desc_t* cache, int tpc) {
     return (PA_CHUNK_TILES > 0 ? PA_CHUNK_TILES : (row_bytes <= 128 ? 4 : 2)) * tpc;
 }
 
+// LDS of one prompt-chunk workgroup: its merge area (static, bounded here from
+// above) and the per-sequence prefix, first query rows and lengths (dynamic).
+size_t chunk_lds_bytes(int num_seqs, int head_dim) {
+    const size_t merge = (size_t)(kChunkWaves - 1) * (head_dim / 16) * kWave * 16 + 2 * (kChunkWaves - 1) * kWave * 4;
+    return merge + 256 + sizeof(int32_t) * (size_t)(3 * num_seqs + 2);
+}
+
 // The persistent grid: resident workgroups per CU times the CUs, or fewer when
 // there are fewer items than that.
 template <int DT, int D, int B>
@@ -2073,7 +2092,7 @@ hipError_t launch_chunk(const DecodeArgs& a, int64_t items, int cus, hipStream_t
     DecodeArgs args_copy = a;
     void* args[] = {&args_copy};
     return hipLaunchKernel(reinterpret_cast<const void*>(&chunk_kernel<DT, D, B>), dim3(grid), dim3(kChunkThreads),
-                           args, sizeof(int32_t) * (size_t)(a.num_seqs + 1), stream);
+                           args, sizeof(int32_t) * (size_t)(3 * a.num_seqs + 2), stream);
 }
 
 hipError_t dispatch_chunk(const DecodeArgs& a, const pa_cache_desc_t* cache, int64_t items, int cus,
@@ -2171,6 +2190,8 @@ pa_status_t decode_impl(const void* q, const void* k_new, const void* v_new, voi
     st = lds_limit(&lds_max);
     if (st != PA_OK) return st;
     if (decode_dynamic_lds(num_seqs, multi, plan.slice) + kDecodeStaticLds > (size_t)lds_max) return PA_ERR_UNSUPPORTED;
+    if (multi && max_query_len > tpc && chunk_lds_bytes(num_seqs, cache->head_dim) > (size_t)lds_max)
+        return PA_ERR_UNSUPPORTED;
 
     hipStream_t sm = static_cast<hipStream_t>(stream);
     if (!multi) {
