@@ -277,7 +277,9 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
  * four waves split the positions and merge at the end: its K/V is read once
  * per block (mostly from L2, the blocks of a sequence running side by side).
  * Preconditions (unchecked): n <= L, and those of pa_decode.  A column whose
- * tokens see no position (only possible when n > L) gives 0.
+ * tokens see no position (only possible when n > L) gives 0.  Limits as in
+ * pa_decode; PA_ERR_UNSUPPORTED also when a workgroup's per-sequence tables
+ * (12 bytes a sequence beside a 25 KB merge area) exceed the device's LDS.
  */
 pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, const int32_t* query_start, float scale, void* out,
