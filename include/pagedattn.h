@@ -134,7 +134,9 @@ pa_status_t pa_write_kv(const void* k_new, const void* v_new, const int64_t* slo
  *                   its first PA_WORKSPACE_SYNC_BYTES bytes must be zero
  *                   before its first use and are left zero by every call;
  *                   the rest needs no initialisation and is clobbered
- * Supported: 1 <= G <= 16, head_dim 64/128, block_size 16/32, num_seqs <= 4096.
+ * Supported: 1 <= G <= 16, head_dim 64/128, block_size 16/32, num_seqs <= 8192
+ * (and per-sequence tables of 8 bytes a sequence within the device's LDS per
+ * workgroup: 160 KB on MI355X), else PA_ERR_UNSUPPORTED.
  * Preconditions (unchecked): 0 <= L <= max_blocks_per_seq * block_size and
  * 0 <= block_tables[s][j] < num_blocks for j < ceil(L / block_size).
  * The result depends only on logical positions: it is bitwise the same
@@ -279,7 +281,8 @@ pa_status_t pa_decode_rope_append(const void* q, const void* k_new, const void* 
  * Preconditions (unchecked): n <= L, and those of pa_decode.  A column whose
  * tokens see no position (only possible when n > L) gives 0.  Limits as in
  * pa_decode; PA_ERR_UNSUPPORTED also when a workgroup's per-sequence tables
- * (12 bytes a sequence beside a 25 KB merge area) exceed the device's LDS.
+ * (16 bytes a sequence, and for prompt chunks 12 beside a 25 KB merge area)
+ * exceed the device's LDS.
  */
 pa_status_t pa_attend(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                       const int32_t* context_lens, const int32_t* query_start, float scale, void* out,

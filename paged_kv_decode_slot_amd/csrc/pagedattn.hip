@@ -57,7 +57,10 @@ constexpr int kWave = 64;
 constexpr int kMaxSlice = PA_MAX_SLICE;            // kv-heads (waves) of one decode workgroup, at most
 constexpr int kGroupThreads = kWave * kMaxSlice;  // the largest decode workgroup
 constexpr int kWriteThreads = 256;
-constexpr int kMaxSeqs = 4096;
+// Sequences one call takes: each decode workgroup keeps 8 (several query
+// tokens: 16) bytes a sequence in LDS, at most 128 KB at this count; the host
+// also checks the device's LDS limit before a launch.
+constexpr int kMaxSeqs = 8192;
 constexpr int kMaxGroup = 16;
 #ifndef PA_WAVES_PER_CU
 #define PA_WAVES_PER_CU 2

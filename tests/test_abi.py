@@ -91,7 +91,7 @@ def test_cache_descriptor_checks(desc, status):
     (dict(bt=None), INVALID), (dict(q=A + 4), INVALID), (dict(out=A + 8), INVALID), (dict(bt=A + 2), INVALID),
     (dict(Hq=3), INVALID), (dict(S=-1), INVALID), (dict(maxblk=-1), INVALID), (dict(Hq=0), INVALID),
     (dict(Hq=34), UNSUPPORTED),  # G = 17
-    (dict(S=4097), UNSUPPORTED),
+    (dict(S=8193), UNSUPPORTED),
     (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID),
     (dict(workers=-2), INVALID),
     (dict(ws=None), WORKSPACE), (dict(ws_bytes=100), WORKSPACE), (dict(ws=A + 16), WORKSPACE),

@@ -225,13 +225,14 @@ def test_attend_negative_scale(dtype):
     assert max_abs_err(out, ref) <= TOL[case.dtype]
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_decode_and_attend_at_the_sequence_cap(D):
-    """4096 sequences (the most one call takes: every workgroup holds per-sequence
-    tables in LDS) through pa_decode_ex and through pa_attend with 8 prompt chunks."""
-    case = W.make_case(S=4096, Hq=8, Hkv=2, D=D, B=16, dtype="bf16", ctx_range=(1, 40), seed=41 + D, name="cap")
+@pytest.mark.parametrize("S,D", [(4096, 64), (8192, 128)])
+def test_decode_and_attend_at_the_sequence_cap(S, D):
+    """Thousands of sequences, up to 8192 (the most one call takes: every workgroup
+    holds per-sequence tables in LDS), through pa_decode_ex and through pa_attend
+    with prompt chunks on every 512th sequence."""
+    case = W.make_case(S=S, Hq=8, Hkv=2, D=D, B=16, dtype="bf16", ctx_range=(1, 40), seed=41 + D, name="cap")
     g = _gpu(case)
-    log(f"[cap] 4096 sequences, D {D}: decode")
+    log(f"[cap] {S} sequences, D {D}: decode")
     out = g.decode(num_workers=0)
     torch.cuda.synchronize()
     kp, vp = oracle.build_pools(case)
@@ -239,7 +240,7 @@ def test_decode_and_attend_at_the_sequence_cap(D):
                  f"[cap] decode D {D}")
     ql = np.where(np.arange(case.S) % 512 == 0, np.minimum(case.context_lens, 20), 1)
     mc = W.with_queries(case, ql, seed=7)
-    log(f"[cap] 4096 sequences, D {D}: attend, q_lens up to {mc.max_q_len}")
+    log(f"[cap] {S} sequences, D {D}: attend, q_lens up to {mc.max_q_len}")
     out = _attend(g, mc)
     torch.cuda.synchronize()
     check_output(out, *_oracle(mc, True), case.dtype, f"[cap] attend D {D}")
