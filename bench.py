@@ -530,7 +530,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this path runs on one GPU (asked for {max(args.gpus, world)}); "
-              "a multi-GPU run is not part of this build.", file=sys.stderr)
+              "runs across several GPUs are not implemented.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -79,7 +79,7 @@ extern "C" {
 typedef enum pa_status {
     PA_OK = 0,
     PA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, Hq not a multiple of Hkv */
-    PA_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
+    PA_ERR_UNSUPPORTED = 2, /* a valid request outside what the library implements */
     PA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
     PA_ERR_HIP = 4,         /* a HIP runtime call or a launch failed */
     PA_ERR_CAPACITY = 5     /* the block pool cannot promise what an admission asks for */
