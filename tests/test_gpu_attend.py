@@ -244,3 +244,34 @@ def test_decode_and_attend_at_the_sequence_cap(S, D):
     out = _attend(g, mc)
     torch.cuda.synchronize()
     check_output(out, *_oracle(mc, True), case.dtype, f"[cap] attend D {D}")
+
+
+def test_attend_graph_replay_matches_eager():
+    """pa_attend with prompt chunks and decode tokens (both launches) captured in a
+    graph: every replay finds the item counters and arrival words at zero again."""
+    case = W.make_case(S=6, Hq=32, Hkv=8, D=128, B=16, dtype="bf16", ctx_range=(300, 2000), seed=941, name="graph")
+    mc = W.with_queries(case, [1, 3, 64, 200, 1, 17], seed=942)
+    g = _gpu(case)
+    q = mc.q.to(DEV)
+    qs = torch.from_numpy(mc.query_start).to(DEV)
+    out = torch.empty_like(q)
+    stream = torch.cuda.Stream()
+    log(f"[attend] graph replay, q_lens {mc.q_lens.tolist()}")
+    with torch.cuda.stream(stream):
+        call = pa.prepare_attend(q, g.k_cache, g.v_cache, g.bt, g.ctx, qs, mc.max_q_len, case.scale, out,
+                                 num_workers=300)
+        call()
+        stream.synchronize()
+        eager = out.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            call()
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dev_bits(out), dev_bits(eager)), f"replay {i}"
+        call()  # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+    assert max_abs_err(eager, _oracle(mc)) <= TOL[case.dtype]
