@@ -164,6 +164,8 @@ CHUNK_SHAPES = [
     # G = 4: 5..8 tokens fill one query block (the chunk kernel's single-block form),
     # 9 and 16 two, 1 goes to the split path
     (dict(S=7, Hq=32, Hkv=8, D=128, B=16, dtype="bf16", ctx_range=(20, 900)), [5, 6, 7, 8, 1, 9, 16]),
+    # G = 2, 64-dim f16 rows (four column tiles: 32 tokens a block), block 32
+    (dict(S=4, Hq=8, Hkv=4, D=64, B=32, dtype="f16", ctx_range=(100, 600)), [9, 40, 1, 100]),
 ]
 
 
