@@ -257,6 +257,7 @@ def measure_chunks(n, args, device):
                 chunk_frac_of_mfma_peak=round(tflops / MFMA_PEAK_TFLOPS[case.dtype], 4),
                 bytes=b, gbs=round(b / (us * 1e-6) / 1e9, 1),
                 chunk_kernel_traffic=None if c is None else c["total"],
+                chunk_kernel_l2_hit_rate=None if c is None else c["l2_hit_rate"],
                 note="one pa_attend call: chunk_kernel for the chunks, the split path for the decode tokens; "
                      "chunk_tflops counts only the chunks' causal FLOPs over the whole call's time, against the "
                      "dense matrix-core peak of the dtype; chunk_kernel_traffic: counter bytes of the chunk "
@@ -402,8 +403,9 @@ KERNEL_SOURCE = "paged_kv_decode_slot_amd/csrc/pagedattn.hip"
 
 
 def measured_counters(config: int, kind: str):
-    """{"fetch", "write", "total"} bytes per launch from a counter summary, or None if
-    there is none or the kernel source changed since it was taken."""
+    """{"fetch", "write", "total"} bytes per launch and the L2 hit rate (None when not
+    taken) from a counter summary, or None if there is none or the kernel source
+    changed since it was taken."""
     import hashlib
 
     path = TRAFFIC_FILES.get((config, kind))
@@ -418,7 +420,13 @@ def measured_counters(config: int, kind: str):
     if fields.get("source_sha256") != src or "traffic_bytes_per_launch" not in fields:
         return None
     fetch, write = [int(x.split()[-1]) for x in fields["scaled bytes per launch"].split(",")]
-    return dict(fetch=fetch, write=write, total=int(fields["traffic_bytes_per_launch"]))
+    hit = float(fields["l2_hit_rate"]) if "l2_hit_rate" in fields else None
+    return dict(fetch=fetch, write=write, total=int(fields["traffic_bytes_per_launch"]), l2_hit_rate=hit)
+
+
+def l2_hit_rate(config: int, kind: str):
+    c = measured_counters(config, kind)
+    return None if c is None else c["l2_hit_rate"]
 
 
 def measured_traffic(config: int, kind: str):
@@ -639,6 +647,7 @@ def main():
             "traffic": measured_traffic(args.config, "fused"),
             "traffic_unit": "bytes per launch",
             "kv_share": kv_share(case, args.config, "fused"),
+            "l2_hit_rate": l2_hit_rate(args.config, "fused"),
             "bytes_per_launch": step_bytes,
             "launch_us_mean": round(main_res["step_us_mean"], 2),
             "timing": "HIP events around the K back-to-back launches on the launch stream",
