@@ -1502,7 +1502,8 @@ __device__ inline void query_rows(const DecodeArgs& a, int i, int& q0, int& nq) 
 template <int DT, int D, int B, bool REUSE>
 __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, int s, int g, int qb, int q0, int nq,
                                                           int L, f32x4 (*s_o)[Cfg<DT, D, B>::kVChunk][kWave],
-                                                          float (*s_m)[kWave], float (*s_l)[kWave]) {
+                                                          float (*s_m)[kWave], float (*s_l)[kWave],
+                                                          unsigned long long* ctr, int lo_item, int32_t* s_item) {
     using C = Cfg<DT, D, B>;
     constexpr int E = C::kElt;
     constexpr int NT = chunk_tiles<DT, D>();
@@ -1656,6 +1657,11 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
     }
     wait_vmem_done();
 
+    // The workgroup's next item is claimed now, so that the claim's round trip
+    // overlaps the merge below; it is published with the merge's last barrier.
+    unsigned long long nxt = 0;
+    if (threadIdx.x == 0) nxt = atomicAdd(ctr, 1ull);
+
     // Merge the four waves' states, one column tile at a time: waves 1..3 put
     // theirs in LDS, wave 0 combines them with its own and stores the output.
 #pragma unroll
@@ -1693,6 +1699,7 @@ __device__ __attribute__((always_inline)) void chunk_item(const DecodeArgs& a, i
                 for (int c = 0; c < C::kVChunk; ++c) store4<DT>(orow + (16 * c + 4 * r) * E, acc[c] * inv);
             }
         }
+        if (ct == NT - 1 && threadIdx.x == 0) *s_item = lo_item + (int)nxt;
         __syncthreads();
     }
 }
@@ -1762,9 +1769,9 @@ __global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chu
     for (int v = 0; v < kXcds; ++v) {
         const int x = (home + v) % kXcds;
         const int lo_item = (int)((int64_t)nitems * x / kXcds), hi_item = (int)((int64_t)nitems * (x + 1) / kXcds);
+        if (tid == 0) s_item = lo_item + (int)atomicAdd(counter + x, 1ull);
+        __syncthreads();
         for (;;) {
-            if (tid == 0) s_item = lo_item + (int)atomicAdd(counter + x, 1ull);
-            __syncthreads();
             const int item = __builtin_amdgcn_readfirstlane(s_item);
             __syncthreads();
             if (item >= hi_item) break;
@@ -1775,9 +1782,11 @@ __global__ __launch_bounds__(kChunkThreads, (chunk_occupancy<DT, D>())) void chu
             const int nq = max(__builtin_amdgcn_readfirstlane(s_q0[s + 1]), q0) - q0;
             const int L = __builtin_amdgcn_readfirstlane(s_len[s]);
             if (nqb > 1)
-                chunk_item<DT, D, B, true>(a, s, local / nqb, local % nqb, q0, nq, L, s_o, s_m, s_l);
+                chunk_item<DT, D, B, true>(a, s, local / nqb, local % nqb, q0, nq, L, s_o, s_m, s_l, counter + x,
+                                           lo_item, &s_item);
             else
-                chunk_item<DT, D, B, false>(a, s, local / nqb, local % nqb, q0, nq, L, s_o, s_m, s_l);
+                chunk_item<DT, D, B, false>(a, s, local / nqb, local % nqb, q0, nq, L, s_o, s_m, s_l, counter + x,
+                                            lo_item, &s_item);
         }
     }
     // The last workgroup out puts the counters (and the count) back to zero.
